@@ -1,0 +1,353 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a closed
+form, an invariant of softmax attention, 50-digit brute force, PyTorch's CPU
+float64 scaled_dot_product_attention, or a number printed on the pages.  The
+set is chosen so that a dropped scale, a flipped mask, a wrong head map, a
+transposed operand, a missing log/max term in lse, a missing rescale in the
+running softmax or a wrong merge weight each fail at least one test; the
+planted-mistake tests at the bottom show that for a few of them.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import exact as oatt
+from exact_tiled_attention_prefill_amd.inputs import decode_inputs, prefill_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape)
+
+
+# ---------------------------------------------------------------- P1 / P13
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(causal):
+    """P1: with V = 1 every output is 1 (softmax weights sum to one)."""
+    q, k = rand((2, 3, 37, 8), 1), rand((2, 3, 37, 8), 2)
+    o, _ = oracle.attention(q, k, np.ones_like(k), causal, 0.7)
+    assert np.abs(o - 1).max() <= 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_convex_hull(causal):
+    """P13: each output coordinate lies between the min and max of the V rows it sees."""
+    q, k, v = rand((1, 2, 29, 5), 3), rand((1, 2, 29, 5), 4), rand((1, 2, 29, 5), 5)
+    o, _ = oracle.attention(q, k, v, causal, 1.3)
+    for i in range(29):
+        vis = v[:, :, : i + 1] if causal else v
+        assert np.all(o[:, :, i] >= vis.min(axis=2) - 1e-15)
+        assert np.all(o[:, :, i] <= vis.max(axis=2) + 1e-15)
+
+
+# ---------------------------------------------------------------- P2 / P3
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean(causal):
+    """P2: all keys equal -> uniform weights -> mean of the visible V rows."""
+    n, d = 23, 6
+    q = rand((1, 1, n, d), 6)
+    k = np.repeat(rand((1, 1, 1, d), 7), n, axis=2)
+    v = rand((1, 1, n, d), 8)
+    o, lse = oracle.attention(q, k, v, causal, 0.9)
+    for i in range(n):
+        vis = v[0, 0, : i + 1] if causal else v[0, 0]
+        assert np.abs(o[0, 0, i] - vis.mean(axis=0)).max() <= 1e-14
+        s = 0.9 * q[0, 0, i] @ k[0, 0, 0]
+        assert abs(lse[0, 0, i] - (s + math.log(len(vis)))) <= 1e-13
+
+
+def test_dominant_key_selects_its_value():
+    """P3: one key whose score exceeds the rest by >= 40 returns its V row."""
+    n, d = 16, 4
+    q = np.zeros((1, 1, n, d))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, n, d))
+    jstar = 11
+    k[0, 0, jstar, 0] = 50.0
+    v = rand((1, 1, n, d), 9)
+    o, lse = oracle.attention(q, k, v, False, 1.0)
+    assert np.abs(o[0, 0] - v[0, 0, jstar]).max() <= 1e-14
+    assert abs(lse[0, 0, 0] - 50.0) <= 1e-14
+
+
+# ---------------------------------------------------------------- P4 / P5
+def test_causal_row0_is_v0():
+    """P4: under the causal mask row 0 sees only key 0: o = V[0], lse = scale q0.k0."""
+    q, k, v = rand((2, 2, 9, 7), 10), rand((2, 2, 9, 7), 11), rand((2, 2, 9, 7), 12)
+    o, lse = oracle.attention(q, k, v, True, 0.37)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    assert np.allclose(lse[:, :, 0], 0.37 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                       rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token(causal):
+    """P5: N = 1 returns V[0] under either mask."""
+    q, k, v = rand((1, 4, 1, 3), 13), rand((1, 2, 1, 3), 14), rand((1, 2, 1, 3), 15)
+    o, _ = oracle.attention(q, k, v, causal, 2.0)
+    assert np.array_equal(o[0, :2, 0], np.repeat(v[0, 0], 2, axis=0).reshape(2, 3))
+    assert np.array_equal(o[0, 2:, 0], np.repeat(v[0, 1], 2, axis=0).reshape(2, 3))
+
+
+# ---------------------------------------------------------------- P6
+def _mp_attention(q, k, v, causal, scale):
+    import mpmath as mp
+
+    mp.mp.dps = 50
+    n, d = q.shape
+    out = []
+    lses = []
+    for i in range(n):
+        js = range(i + 1) if causal else range(n)
+        s = [mp.mpf(scale) * mp.fsum(mp.mpf(q[i, c]) * mp.mpf(k[j, c]) for c in range(d)) for j in js]
+        e = [mp.e ** x for x in s]
+        tot = mp.fsum(e)
+        out.append([mp.fsum(e[t] * mp.mpf(v[j, c]) for t, j in enumerate(js)) / tot for c in range(d)])
+        lses.append(mp.log(tot))
+    return np.array(out, dtype=object), np.array(lses, dtype=object)
+
+
+@pytest.mark.parametrize("d", [1, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mpmath_bruteforce_4x4(d, causal):
+    """P6: hand-sized cases against a 50-digit evaluation of the definition."""
+    g = np.random.default_rng(100 + d + 10 * causal)
+    # values exactly representable in bf16 (multiples of 1/8 in [-4, 4])
+    q = g.integers(-32, 33, (4, d)) / 8.0
+    k = g.integers(-32, 33, (4, d)) / 8.0
+    v = g.integers(-32, 33, (4, d)) / 8.0
+    scale = 0.5
+    o, lse = oracle.attention(q[None, None], k[None, None], v[None, None], causal, scale)
+    mo, ml = _mp_attention(q, k, v, causal, scale)
+    assert np.abs(o[0, 0] - mo.astype(float)).max() <= 1e-14
+    assert np.abs(lse[0, 0] - ml.astype(float)).max() <= 1e-14
+
+
+# ---------------------------------------------------------------- P7
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(1, 1), (3, 5), (64, 64), (16, 7), (70, 70)])
+def test_tiled_running_softmax_equals_full(causal, bq, bk):
+    """P7: tile-by-tile running softmax == materialised softmax (exactness claim)."""
+    q, k, v = rand((2, 4, 70, 16), 20), rand((2, 2, 70, 16), 21), rand((2, 2, 70, 16), 22)
+    o, lse = oracle.attention(q, k, v, causal, 0.25)
+    ot, lt = oracle.tiled_attention(q, k, v, causal, 0.25, bq, bk)
+    assert np.abs(o - ot).max() <= 1e-12
+    assert np.abs(lse - lt).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P8
+@pytest.mark.parametrize("cuts", [[40], [1, 2, 90], [17, 34, 51, 68], [0, 100, 120]])
+def test_split_merge_equals_all_keys(cuts):
+    """P8: attention over disjoint key chunks merged by lse weights == over all keys."""
+    n, d = 128, 8
+    q = rand((3, 4, d), 30)
+    kc, vc = rand((3, 2, n, d), 31), rand((3, 2, n, d), 32)
+    lens = [n, n, n]
+    full_o, full_lse = oracle.decode(q, kc, vc, lens, 0.3)
+    edges = [0] + cuts + [n]
+    parts_o, parts_l = [], []
+    for a, b in zip(edges[:-1], edges[1:]):
+        sub_k = kc[:, :, a:b]
+        sub_v = vc[:, :, a:b]
+        o_s, l_s = oracle.decode(q, sub_k, sub_v, [b - a] * 3, 0.3)
+        parts_o.append(o_s)
+        parts_l.append(l_s)
+    mo, ml = oracle.merge_partials(np.stack(parts_o), np.stack(parts_l))
+    assert np.abs(mo - full_o).max() <= 1e-12
+    assert np.abs(ml - full_lse).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P9
+def test_decode_equals_last_causal_prefill_row():
+    """P9: decode of token i against cache 0..i == causal prefill row i."""
+    n, d = 33, 8
+    q, k, v = rand((2, 4, n, d), 40), rand((2, 2, n, d), 41), rand((2, 2, n, d), 42)
+    o, lse = oracle.attention(q, k, v, True, 0.5)
+    for i in (0, 5, 31, 32):
+        od, ld = oracle.decode(q[:, :, i], k, v, [i + 1, i + 1], 0.5)
+        assert np.abs(od - o[:, :, i]).max() <= 1e-12
+        assert np.abs(ld - lse[:, :, i]).max() <= 1e-12
+
+
+def test_decode_never_reads_past_length():
+    """Cache rows at or past seqlens[b] hold NaN; the result stays finite."""
+    q, kc, vc, lens, scale = decode_inputs(3, 4, 2, 8, 1, 9, 12, "bf16", seed=3)
+    o, lse = oracle.decode(q, kc, vc, lens, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    q2 = q.clone()
+    o0, l0 = oracle.decode(q2, kc, vc, [0, 1, 2], scale)
+    assert np.all(o0[0] == 0) and np.all(np.isneginf(l0[0]))
+    # sequence 1 has one visible entry: every head returns its V row 0
+    for h in range(4):
+        assert np.array_equal(o0[1, h], vc[1, h // 2, 0].double().numpy())
+
+
+# ---------------------------------------------------------------- P10
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_mha_with_repeated_heads(causal):
+    """P10: GQA with G = Hq/Hkv equals MHA on K/V heads repeated G times consecutively."""
+    q, k, v = rand((2, 8, 19, 4), 50), rand((2, 2, 19, 4), 51), rand((2, 2, 19, 4), 52)
+    og, lg = oracle.attention(q, k, v, causal, 0.6)
+    om, lm = oracle.attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), causal, 0.6)
+    assert np.array_equal(og, om) and np.array_equal(lg, lm)
+
+
+# ---------------------------------------------------------------- P11 / P12
+def test_permutation_symmetry_noncausal():
+    """P11: jointly permuting K,V rows changes nothing; permuting Q permutes O."""
+    q, k, v = rand((1, 2, 31, 6), 60), rand((1, 2, 31, 6), 61), rand((1, 2, 31, 6), 62)
+    o, lse = oracle.attention(q, k, v, False, 0.8)
+    perm = np.random.default_rng(63).permutation(31)
+    o2, l2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], False, 0.8)
+    assert np.abs(o - o2).max() <= 1e-13 and np.abs(lse - l2).max() <= 1e-13
+    o3, l3 = oracle.attention(q[:, :, perm], k, v, False, 0.8)
+    assert np.abs(o[:, :, perm] - o3).max() <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_affine_equivariance(causal):
+    """P12: O(V A + 1 b^T) = O(V) A + b^T because the weights sum to one."""
+    q, k, v = rand((1, 1, 25, 5), 70), rand((1, 1, 25, 5), 71), rand((1, 1, 25, 5), 72)
+    a, bvec = rand((5, 5), 73), rand((5,), 74)
+    o, _ = oracle.attention(q, k, v, causal, 0.4)
+    o2, _ = oracle.attention(q, k, v @ a + bvec, causal, 0.4)
+    assert np.abs(o2 - (o @ a + bvec)).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P14 / P15
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_bounds_and_zero_scale(causal):
+    """P14: max s <= lse <= max s + ln|J|; scale 0 -> lse = ln|J|, o = mean."""
+    n = 21
+    q, k, v = rand((1, 2, n, 4), 80), rand((1, 2, n, 4), 81), rand((1, 2, n, 4), 82)
+    o, lse = oracle.attention(q, k, v, causal, 0.9)
+    for h in range(2):
+        s = oracle.score_matrix(q[0, h], k[0, h], 0.9, causal)
+        m = s.max(axis=1)
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        assert np.all(lse[0, h] >= m - 1e-14) and np.all(lse[0, h] <= m + np.log(cnt) + 1e-14)
+    o0, l0 = oracle.attention(q, k, v, causal, 0.0)
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    assert np.abs(l0[0] - np.log(cnt)[None]).max() <= 1e-14
+    means = np.cumsum(v[0], axis=1) / cnt[None, :, None] if causal else np.broadcast_to(v[0].mean(axis=1, keepdims=True), v[0].shape)
+    assert np.abs(o0[0] - means).max() <= 1e-14
+
+
+def test_large_scores_are_stable():
+    """P15: scores near 1e3 do not overflow; the result matches the rescaled closed form."""
+    q = np.zeros((1, 1, 4, 2))
+    q[..., 0] = 30.0
+    k = np.zeros((1, 1, 4, 2))
+    k[0, 0, :, 0] = [40.0, 40.0, 39.0, 0.0]  # scores 1200, 1200, 1170, 0
+    v = rand((1, 1, 4, 2), 90)
+    o, lse = oracle.attention(q, k, v, False, 1.0)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    w = np.array([1.0, 1.0, math.exp(-30.0), math.exp(-1200.0)])
+    ref = (w[:, None] * v[0, 0]).sum(0) / w.sum()
+    assert np.abs(o[0, 0] - ref).max() <= 1e-14
+    assert abs(lse[0, 0, 0] - (1200.0 + math.log(w.sum()))) <= 1e-12
+
+
+# ---------------------------------------------------------------- P16
+@settings(max_examples=25, deadline=None)
+@given(B=st.integers(1, 2), hkv=st.integers(1, 3), G=st.sampled_from([1, 2, 4]),
+       n=st.integers(1, 70), d=st.sampled_from([1, 4, 64]), causal=st.booleans(),
+       scale=st.floats(0.01, 2.0), seed=st.integers(0, 2**16))
+def test_matches_torch_sdpa_float64(B, hkv, G, n, d, causal, scale, seed):
+    """P16: PyTorch CPU float64 SDPA (is_causal, enable_gqa, scale=) agrees on small shapes."""
+    hq = hkv * G
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, hq, n, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, hkv, n, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, hkv, n, d, generator=g, dtype=torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=causal, scale=scale, enable_gqa=True).numpy()
+    o, _ = oracle.attention(q.numpy(), k.numpy(), v.numpy(), causal, scale)
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+def test_rows_variant_matches_full():
+    """attention_rows evaluates the same definition at chosen rows and heads."""
+    q, k, v, scale = prefill_inputs(2, 4, 2, 50, 16, "bf16", seed=5)
+    o, lse = oracle.attention(q, k, v, True, scale)
+    rows = [0, 1, 17, 48, 49]
+    heads = [(0, 0), (1, 3), (0, 2)]
+    orr, lr = oracle.attention_rows(q, k, v, True, scale, rows, heads)
+    for t, (b, h) in enumerate(heads):
+        assert np.abs(orr[t] - o[b, h, rows]).max() <= 1e-13
+        assert np.abs(lr[t] - lse[b, h, rows]).max() <= 1e-13
+    on, ln_ = oracle.attention_rows(q, k, v, False, scale, rows, heads)
+    of, lf = oracle.attention(q, k, v, False, scale)
+    for t, (b, h) in enumerate(heads):
+        assert np.abs(on[t] - of[b, h, rows]).max() <= 1e-13
+
+
+# ---------------------------------------------------------------- printed numbers
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def test_score_matrix_has_n_squared_entries():
+    """The materialised score matrix has the sizes the pages print (1k -> 1M, 8k -> 64M)."""
+    for tokens, entries in _golden("score_matrix_entries.txt"):
+        x = np.zeros((tokens, 1))
+        s = oracle.score_matrix(x, x, 1.0, False)
+        assert s.size == entries
+        del s
+
+
+def test_gemm_tiling_traffic_matches_page():
+    """Page-1 tiled-GEMM load counts (25 tiles -> 650 loads / 26000 MiB; 13 -> 182 / 14560)."""
+    for tiles, mib, loads, total in _golden("gemm_tiling_traffic.txt"):
+        assert oracle.tiled_gemm_reads(tiles, mib) == (loads, total)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _planted(monkeypatch, fn):
+    monkeypatch.setattr(oatt, "score_matrix", fn)
+
+
+def test_pins_catch_dropped_scale(monkeypatch):
+    real = oatt.score_matrix
+    _planted(monkeypatch, lambda q, k, scale, causal: real(q, k, 1.0, causal))
+    q, k, v = (torch.randn(1, 1, 6, 4, dtype=torch.float64) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=0.3).numpy()
+    o, _ = oracle.attention(q.numpy(), k.numpy(), v.numpy(), False, 0.3)
+    assert np.abs(o - ref).max() > 1e-6
+
+
+def test_pins_catch_flipped_causal_mask(monkeypatch):
+    def flipped(q, k, scale, causal):
+        s = float(scale) * (np.asarray(q, float) @ np.asarray(k, float).T)
+        if causal:
+            s[np.tril(np.ones(s.shape, dtype=bool), k=-1)] = -np.inf
+        return s
+    _planted(monkeypatch, flipped)
+    q, k, v = rand((1, 1, 9, 7), 10), rand((1, 1, 9, 7), 11), rand((1, 1, 9, 7), 12)
+    o, _ = oracle.attention(q, k, v, True, 0.37)
+    assert not np.array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_pins_catch_wrong_head_map(monkeypatch):
+    monkeypatch.setattr(oatt, "_kv_head", lambda h, hq, hkv: h % hkv)
+    g = torch.Generator().manual_seed(1)
+    q = torch.randn(1, 4, 5, 3, generator=g, dtype=torch.float64)
+    k = torch.randn(1, 2, 5, 3, generator=g, dtype=torch.float64)
+    v = torch.randn(1, 2, 5, 3, generator=g, dtype=torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, enable_gqa=True).numpy()
+    o, _ = oracle.attention(q.numpy(), k.numpy(), v.numpy(), False, 1 / math.sqrt(3))
+    assert np.abs(o - ref).max() > 1e-6

@@ -1,6 +1,198 @@
-"""placeholder; replaced by the ctypes binding"""
+"""ctypes binding of libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback -- if libfa.so is missing or the
+device is unsupported, the call raises.
+"""
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa.so"
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_ERR_NO_MEMORY = 4
+
+# name -> (restype, argtypes); the exported symbols of include/fa.h
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_strerror": (ctypes.c_char_p, [_i]),
+    "fa_version": (_i, []),
+    "fa_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_prefill_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_decode_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_decode_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_decode_f32_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
 class FaError(RuntimeError):
-    pass
-def _missing(*a, **k):
-    raise FaError("libfa.so not built")
-decode = decode_workspace_bytes = library_path = load_library = prefill = _missing
+    """A libfa call returned a non-zero fa_status."""
+
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+
+
+def library_path():
+    return os.environ.get("FA_LIBRARY", os.path.join(PKG, _LIB_NAME))
+
+
+def load_library():
+    """Load libfa.so once and declare every exported signature."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise FaError(-1, f"{path} not found; build it with "
+                                  "`python -m exact_tiled_attention_prefill_amd.build`")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def strerror(status):
+    if status == -1:
+        return "library not built"
+    try:
+        return load_library().fa_strerror(int(status)).decode()
+    except Exception:  # library unavailable: plain code
+        return f"fa_status {status}"
+
+
+def _check(status, what):
+    if status != FA_OK:
+        raise FaError(status, what)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True, stream=None):
+    """Exact attention softmax(scale*QK^T + mask)V on the GPU.
+
+    q [B,Hq,N,d], k/v [B,Hkv,N,d]: contiguous device tensors, all bf16 or
+    all float32.  Returns (o, lse) with o like q and lse float32 [B,Hq,N]
+    (lse is None when return_lse=False and no lse buffer is given).
+    """
+    torch = _torch()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype, 4)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, N):
+            raise ValueError("lse must be [B, Hq, N]")
+    lib = load_library()
+    fn = lib.fa_prefill if dtype == torch.bfloat16 else lib.fa_prefill_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if lse is not None else None,
+            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_ptr(stream))
+    _check(st, "fa_prefill" if dtype == torch.bfloat16 else "fa_prefill_f32")
+    return out, lse
+
+
+def decode_workspace_bytes(B, Hq, Hkv, maxlen, d):
+    return int(load_library().fa_decode_workspace_bytes(B, Hq, Hkv, maxlen, d))
+
+
+def decode(q, kcache, vcache, seqlens, scale=None, out=None, workspace=None, stream=None):
+    """One query token per sequence against a contiguous KV cache.
+
+    q [B,Hq,d]; kcache/vcache [B,Hkv,maxlen,d] (bf16 or float32, matching q);
+    seqlens int32 [B] on the device.  `workspace` (uint8 device tensor of at
+    least decode_workspace_bytes(...) bytes) avoids the library's
+    stream-ordered allocation.  Returns o [B,Hq,d].
+    """
+    torch = _torch()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/kcache/vcache must be bfloat16 or float32")
+    _require(q, "q", dtype, 3)
+    _require(kcache, "kcache", dtype, 4)
+    _require(vcache, "vcache", dtype, 4)
+    _require(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, d = q.shape
+    _, Hkv, maxlen, _ = kcache.shape
+    if tuple(kcache.shape) != (B, Hkv, maxlen, d) or tuple(vcache.shape) != (B, Hkv, maxlen, d):
+        raise ValueError("kcache/vcache must be [B, Hkv, maxlen, d] matching q")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must be [B]")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype, 3)
+    lib = load_library()
+    args = (_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B, Hq, Hkv, maxlen, d,
+            float(scale))
+    bf16 = dtype == torch.bfloat16
+    if workspace is None:
+        fn = lib.fa_decode if bf16 else lib.fa_decode_f32
+        st = fn(*args, _stream_ptr(stream))
+    else:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+            raise TypeError("workspace must be a uint8 device tensor")
+        fn = lib.fa_decode_ws if bf16 else lib.fa_decode_f32_ws
+        st = fn(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    _check(st, fn.__name__)
+    return out

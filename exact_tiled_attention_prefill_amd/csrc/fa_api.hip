@@ -1,0 +1,177 @@
+// C-ABI layer of libfa.so: argument validation, device check, dispatch.
+// Every check that can fail on arguments alone runs before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+int g_arch_state[kMaxDevices] = {0};
+std::mutex g_arch_mutex;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_arch_mutex);
+  if (g_arch_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+    const char* want = "gfx950";
+    bool ok = true;
+    for (int i = 0; want[i] != '\0'; ++i)
+      if (prop.gcnArchName[i] != want[i]) ok = false;
+    g_arch_state[dev] = ok ? 1 : 2;
+  }
+  return g_arch_state[dev] == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+float softmax_coeff(float scale) {
+  float c = std::fabs(scale) * fa::kLog2e;
+  return c < fa::kMinC ? fa::kMinC : c;
+}
+
+int check_common(int B, int Hq, int Hkv, int d, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int prefill_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale, void* stream, bool bf16) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (N <= 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  // grid limits: B*Hq*ceil(N/rows) workgroups must fit in 31 bits
+  if ((long long)B * Hq * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_coeff(scale), scale < 0.f};
+  hipError_t e = bf16 ? fa::launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
+                      : fa::launch_prefill_f32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int decode_check(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o, int B,
+                 int Hq, int Hkv, int maxlen, int d, float scale) {
+  if (q == nullptr || kc == nullptr || vc == nullptr || seqlens == nullptr || o == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (maxlen <= 0) return FA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, d, scale);
+  if (st != FA_OK) return st;
+  if (B > 65535 || Hq > 65535) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(o, 16) || !aligned(seqlens, 4))
+    return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int decode_run(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o, int B, int Hq,
+               int Hkv, int maxlen, int d, float scale, void* ws, size_t ws_bytes, void* stream, bool bf16) {
+  int st = decode_check(q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa::decode_workspace_bytes(B, Hq, maxlen, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool owned = false;
+  if (ws != nullptr) {
+    if (ws_bytes < need || !aligned(ws, 256)) return FA_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != FA_OK) return st;
+  } else {
+    st = check_device();
+    if (st != FA_OK) return st;
+    if (hipMallocAsync(&ws, need, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_NO_MEMORY;
+    }
+    owned = true;
+  }
+  fa::DecodeArgs a{q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, softmax_coeff(scale), scale < 0.f, ws};
+  hipError_t e = bf16 ? fa::launch_decode_bf16(a, s) : fa::launch_decode_f32(a, s);
+  if (owned) {
+    hipError_t f = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK: success";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dimension or device not supported";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP: HIP runtime or launch failure";
+    case FA_ERR_NO_MEMORY:
+      return "FA_ERR_NO_MEMORY: workspace allocation failed";
+    default:
+      return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+               int N, int d, int causal, float scale, void* stream) {
+  return prefill_common(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, true);
+}
+
+int fa_prefill_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale, void* stream) {
+  return prefill_common(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, false);
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || maxlen <= 0 || (d != 64 && d != 128) || Hq % Hkv != 0) return 0;
+  return fa::decode_workspace_bytes(B, Hq, maxlen, d);
+}
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,
+              int Hq, int Hkv, int maxlen, int d, float scale, void* stream) {
+  return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, nullptr, 0, stream, true);
+}
+
+int fa_decode_ws(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o,
+                 int B, int Hq, int Hkv, int maxlen, int d, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return FA_ERR_INVALID_ARG;
+  return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, workspace, workspace_bytes,
+                    stream, true);
+}
+
+int fa_decode_f32(const float* q, const float* kcache, const float* vcache, const int32_t* seqlens, float* o,
+                  int B, int Hq, int Hkv, int maxlen, int d, float scale, void* stream) {
+  return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, nullptr, 0, stream, false);
+}
+
+int fa_decode_f32_ws(const float* q, const float* kcache, const float* vcache, const int32_t* seqlens,
+                     float* o, int B, int Hq, int Hkv, int maxlen, int d, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return FA_ERR_INVALID_ARG;
+  return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, workspace, workspace_bytes,
+                    stream, false);
+}
+
+}  // extern "C"

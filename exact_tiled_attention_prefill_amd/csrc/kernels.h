@@ -1,0 +1,51 @@
+// Internal launch interface between the C-ABI layer (fa_api.hip) and the
+// kernels.  All sizes are validated by the caller; pointers are device memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Softmax runs in base 2: exp(scale*s) = exp2(c*s) with c = |scale|*log2(e),
+// and a negative scale is applied by flipping the sign of q (exact).  c is
+// clamped below at kMinC so that c*(-inf) stays -inf (a zero scale would
+// otherwise turn masked scores into NaN); at that size c*s rounds every
+// exponent of a finite score to 0 exactly as a zero scale would.
+constexpr float kMinC = 1e-30f;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float c;       // |scale| * log2(e), >= kMinC
+  bool neg;      // scale < 0: use -q
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens;
+  void* o;
+  int B, Hq, Hkv, maxlen, d;
+  float c;
+  bool neg;
+  void* ws;  // >= decode_workspace_bytes(...)
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+
+// Keys per split-KV chunk in decode.
+constexpr int kDecodeChunk = 512;
+size_t decode_workspace_bytes(int B, int Hq, int maxlen, int d);
+
+}  // namespace fa

@@ -1,0 +1,136 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled attention on AMD MI355X (gfx950).
+ *
+ * What is computed.  For every batch b, query head h and query row i:
+ *
+ *     o[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,g,j,:] ) * v[b,g,j,:]
+ *     lse[b,h,i] = log sum_j exp( scale * q[b,h,i,:] . k[b,g,j,:] )
+ *
+ * with g = h / (Hq/Hkv) (grouped-query attention: consecutive query heads
+ * share one key/value head), and j running over all keys, or over j <= i
+ * under the causal mask.  This is softmax(Q K^T) V as written in the forum
+ * comment on SRAM and GEMM tiling (item 45450456, paragraph on KV caching),
+ * with the scale and mask between score and normalisation as listed in
+ * "How Does Flash Attention Reduce Memory Traffic During Local Inference?",
+ * section "Kernel Fusion Keeps More of the Attention Chain in One Execution
+ * Path", and the GQA head sharing of "Optimizing memory requirements for
+ * inference in large language models" (GQA paragraph).  The result is exact
+ * up to floating-point rounding ("11.4d FlashAttention", comparison table):
+ * it is computed tile by tile with a running softmax ("11.4d FlashAttention",
+ * "Online Softmax") so no N x N score matrix is ever written to memory.
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     reads/writes them asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream) and keeps no reference after the enqueued work completes.
+ *     The caller keeps the buffers alive until then.
+ *   - Tensors are dense row-major (C-contiguous) with the layouts given per
+ *     call; bf16 tensors are passed as raw 16-bit storage (bfloat16).
+ *     bf16 and fp32 tensor pointers must be 16-byte aligned; lse and seqlens
+ *     4-byte aligned.
+ *   - No call synchronises the host.  Faults inside a kernel surface at the
+ *     caller's next synchronisation on `stream`.
+ *   - Status codes (fa_status) are returned, never thrown.  All argument
+ *     checks run on the host before any HIP call, so invalid arguments never
+ *     touch the device.
+ *   - Head dimension d must be 64 or 128 (FA_ERR_UNSUPPORTED otherwise), and
+ *     the current device must be gfx950 (FA_ERR_UNSUPPORTED otherwise).  There
+ *     is no silent fallback: the caller decides what to do.
+ *   - Calls are thread-safe; the library holds no mutable global state other
+ *     than a per-device architecture cache.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, Hq % Hkv != 0, non-finite
+                             scale, misaligned pointer, too-small workspace */
+  FA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, or device is not gfx950 */
+  FA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  FA_ERR_NO_MEMORY = 4    /* stream-ordered workspace allocation failed */
+} fa_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_strerror(int status);
+
+/*
+ * Prefill (bf16 in/out, fp32 accumulation and lse).
+ *   q   [B, Hq,  N, d]  bf16      k, v [B, Hkv, N, d]  bf16
+ *   o   [B, Hq,  N, d]  bf16 (written)
+ *   lse [B, Hq,  N]     fp32 (written; may be NULL to skip)
+ *   causal: 0 = every query sees every key; 1 = query i sees keys 0..i.
+ *   scale: multiplies q.k before the mask and softmax (finite; any sign).
+ * Work: one kernel launch on `stream`.
+ */
+int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               void* stream);
+
+/* Prefill with fp32 q/k/v/o (same layouts and semantics; fp32 arithmetic). */
+int fa_prefill_f32(const float* q, const float* k, const float* v, float* o,
+                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                   float scale, void* stream);
+
+/*
+ * Decode: one new query token per sequence against its KV cache.  The cache
+ * grows with the context and is retained by the caller between steps; this
+ * call only reads it ("How Does Flash Attention Reduce Memory Traffic ...",
+ * section "Reduced IO Is Not the Same as Eliminating KV Cache").  Each step
+ * re-reads the whole cache of each sequence including the newest entry
+ * (forum comment item 45450456, paragraph on KV caching).
+ *   q       [B, Hq, d]              bf16
+ *   kcache  [B, Hkv, maxlen, d]     bf16 (one contiguous maxlen x d slab per
+ *   vcache  [B, Hkv, maxlen, d]     bf16  sequence and key/value head)
+ *   seqlens [B]                     int32, device memory; sequence b attends
+ *                                   to cache rows 0 .. seqlens[b]-1, which
+ *                                   already include the new token.  Rows at or
+ *                                   past seqlens[b] are never read.  Values
+ *                                   are clamped to [0, maxlen] on the device;
+ *                                   seqlens[b] == 0 gives o = 0.
+ *   o       [B, Hq, d]              bf16 (written)
+ * The key range is split into chunks whose partial results are merged by
+ * their log-sum-exp weights.  fa_decode obtains that workspace stream-ordered
+ * (hipMallocAsync / hipFreeAsync on `stream`); fa_decode_ws takes it from
+ * the caller instead (at least fa_decode_workspace_bytes(...) bytes, 256-byte
+ * aligned, device memory, not used concurrently by another call).
+ * Work: two kernel launches on `stream`; the host never reads seqlens.
+ */
+int fa_decode(const void* q, const void* kcache, const void* vcache,
+              const int32_t* seqlens, void* o, int B, int Hq, int Hkv,
+              int maxlen, int d, float scale, void* stream);
+
+int fa_decode_ws(const void* q, const void* kcache, const void* vcache,
+                 const int32_t* seqlens, void* o, int B, int Hq, int Hkv,
+                 int maxlen, int d, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Decode with fp32 q/caches/o (same layouts and semantics). */
+int fa_decode_f32(const float* q, const float* kcache, const float* vcache,
+                  const int32_t* seqlens, float* o, int B, int Hq, int Hkv,
+                  int maxlen, int d, float scale, void* stream);
+
+int fa_decode_f32_ws(const float* q, const float* kcache, const float* vcache,
+                     const int32_t* seqlens, float* o, int B, int Hq, int Hkv,
+                     int maxlen, int d, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_decode_ws / fa_decode_f32_ws need for these sizes
+ * (0 if the sizes are invalid). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,156 @@
+"""The C ABI on a host without a GPU: the library loads, exports exactly what
+include/fa.h declares, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_tiled_attention_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(binding.library_path()),
+                               reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fa_prefill", "fa_decode", "fa_prefill_f32", "fa_decode_f32", "fa_decode_ws",
+              "fa_decode_f32_ws", "fa_decode_workspace_bytes", "fa_strerror", "fa_version"):
+        assert n in names
+    assert set(names) == set(binding.SIGNATURES)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_[a-z0-9_]+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+@needs_lib
+def test_strerror_and_version():
+    lib = binding.load_library()
+    for code in range(5):
+        assert lib.fa_strerror(code).decode().startswith("FA_")
+    assert b"unknown" in lib.fa_strerror(99)
+    assert lib.fa_version() >= 100
+
+
+P = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails validation first
+P_MIS = ctypes.c_void_p(0x10002)
+
+
+def prefill_call(fn, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, N=16, d=128, causal=1, scale=0.1)
+    a.update(kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+              a["causal"], ctypes.c_float(a["scale"]), None)
+
+
+@needs_lib
+@pytest.mark.parametrize("name", ["fa_prefill", "fa_prefill_f32"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k=None), binding.FA_ERR_INVALID_ARG),
+    (dict(v=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), binding.FA_ERR_INVALID_ARG),
+    (dict(N=-5), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=0), binding.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(q=P_MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(o=P_MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p(0x10001)), binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+    (dict(d=256), binding.FA_ERR_UNSUPPORTED),
+    (dict(d=32), binding.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects_invalid_arguments(name, kw, code):
+    fn = getattr(binding.load_library(), name)
+    assert prefill_call(fn, **kw) == code
+
+
+def decode_call(fn, ws=False, **kw):
+    a = dict(q=P, k=P, v=P, sl=P, o=P, B=2, Hq=8, Hkv=2, maxlen=1024, d=128, scale=0.1,
+             w=P, wb=1 << 30)
+    a.update(kw)
+    args = [a["q"], a["k"], a["v"], a["sl"], a["o"], a["B"], a["Hq"], a["Hkv"], a["maxlen"], a["d"],
+            ctypes.c_float(a["scale"])]
+    if ws:
+        args += [a["w"], a["wb"]]
+    return fn(*args, None)
+
+
+@needs_lib
+@pytest.mark.parametrize("name", ["fa_decode", "fa_decode_f32", "fa_decode_ws", "fa_decode_f32_ws"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k=None), binding.FA_ERR_INVALID_ARG),
+    (dict(v=None), binding.FA_ERR_INVALID_ARG),
+    (dict(sl=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(maxlen=0), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=8, Hkv=3), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(k=P_MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(sl=ctypes.c_void_p(0x10001)), binding.FA_ERR_INVALID_ARG),
+    (dict(B=70000), binding.FA_ERR_INVALID_ARG),
+    (dict(d=80), binding.FA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_invalid_arguments(name, kw, code):
+    fn = getattr(binding.load_library(), name)
+    assert decode_call(fn, ws=name.endswith("_ws"), **kw) == code
+
+
+@needs_lib
+@pytest.mark.parametrize("name", ["fa_decode_ws", "fa_decode_f32_ws"])
+def test_decode_ws_rejects_small_or_missing_workspace(name):
+    lib = binding.load_library()
+    fn = getattr(lib, name)
+    need = lib.fa_decode_workspace_bytes(2, 8, 2, 1024, 128)
+    assert need > 0
+    assert decode_call(fn, ws=True, w=None) == binding.FA_ERR_INVALID_ARG
+    assert decode_call(fn, ws=True, wb=need - 1) == binding.FA_ERR_INVALID_ARG
+    assert decode_call(fn, ws=True, w=ctypes.c_void_p(0x10010)) == binding.FA_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_workspace_bytes():
+    lib = binding.load_library()
+    # two fp32 partial arrays: [B,Hq,nsplit,d] and [B,Hq,nsplit], each padded to 256 bytes
+    nsplit = (32768 + 511) // 512
+    po = 64 * 32 * nsplit * 128 * 4
+    pl = 64 * 32 * nsplit * 4
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 128) == rnd(po) + rnd(pl)
+    assert lib.fa_decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
+    assert lib.fa_decode_workspace_bytes(64, 32, 5, 32768, 128) == 0
+    assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 96) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("FA_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(binding.FaError):
+        binding.load_library()

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test draws seeded inputs on the CPU, runs libfa on the GPU and compares
+element by element with the oracle on the same values.  Tolerances: fp32
+max-abs 1e-5; bf16 max-abs 2e-2 and mean-abs 2e-3 on O, 1e-3 on lse.
+The full-size workloads are checked on sampled rows (the oracle evaluates
+those rows one by one) plus properties on every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_prefill_amd import decode, decode_workspace_bytes, prefill
+from exact_tiled_attention_prefill_amd import inputs as I
+from gpu_util import (BF16_LSE_MAX_ABS, F32_LSE_MAX_ABS, F32_MAX_ABS, check_bf16, check_close, f64,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(q, k, v, causal, scale):
+    qd, kd, vd = to_dev(q, k, v)
+    o, lse = prefill(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def gpu_decode(q, kc, vc, lens, scale, workspace=False):
+    qd, kd, vd, ld = to_dev(q, kc, vc, lens)
+    ws = None
+    if workspace:
+        B, Hq, d = q.shape
+        ws = torch.empty(decode_workspace_bytes(B, Hq, kc.shape[1], kc.shape[2], d), dtype=torch.uint8,
+                         device="cuda")
+    o = decode(qd, kd, vd, ld, scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+# ------------------------------------------------------------------ fp32
+def test_fp32_noncausal_workload():
+    """B1 H1 N256 d64 fp32 non-causal, seed 0: max-abs <= 1e-5 on O and lse."""
+    cfg = I.PREFILL_F32_SMALL
+    q, k, v, scale = I.prefill_config_inputs(cfg)
+    o, lse = gpu_prefill(q, k, v, cfg.causal, scale)
+    ro, rl = oracle.attention(q, k, v, cfg.causal, scale)
+    check_close(o, ro, F32_MAX_ABS, "o")
+    check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
+
+
+@pytest.mark.parametrize("N", [1, 5, 127, 128, 129, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_prefill_shapes(N, d, causal):
+    q, k, v, scale = I.prefill_inputs(2, 4, 2, N, d, "f32", seed=N + d)
+    o, lse = gpu_prefill(q, k, v, causal, scale)
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    check_close(o, ro, F32_MAX_ABS, "o")
+    check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
+
+
+# ------------------------------------------------------------------ bf16 prefill, small
+SMALL = [  # (B, Hkv, G, N, d)
+    (1, 1, 1, 1, 128), (1, 1, 1, 2, 64), (2, 1, 2, 63, 128), (1, 2, 1, 64, 64), (1, 1, 4, 65, 128),
+    (2, 2, 1, 127, 128), (1, 1, 8, 128, 64), (1, 2, 2, 129, 128), (1, 1, 1, 255, 128),
+    (1, 1, 4, 256, 128), (2, 1, 1, 257, 64), (1, 2, 4, 1000, 128), (1, 1, 2, 1000, 64),
+    (1, 1, 1, 513, 128), (1, 2, 8, 777, 128),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,G,N,d", SMALL)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_prefill_shapes(B, Hkv, G, N, d, causal):
+    q, k, v, scale = I.prefill_inputs(B, Hkv * G, Hkv, N, d, "bf16", seed=7 * N + d + G)
+    o, lse = gpu_prefill(q, k, v, causal, scale)
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    check_bf16(o, ro, "o")
+    check_close(lse, rl, BF16_LSE_MAX_ABS, "lse")
+
+
+def test_bf16_causal_row0_is_exact():
+    """Causal row 0 sees only key 0: o must equal V[0] bit for bit."""
+    q, k, v, scale = I.prefill_inputs(2, 8, 2, 300, 128, "bf16", seed=11)
+    o, lse = gpu_prefill(q, k, v, True, scale)
+    g = torch.arange(8) // 4
+    assert torch.equal(o[:, :, 0], v[:, g, 0])
+    ref = scale * (f64(q[:, :, 0]) * f64(k[:, g, 0])).sum(-1)
+    assert np.abs(f64(lse[:, :, 0]) - ref).max() <= BF16_LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 3.0])
+def test_bf16_scale_sign_zero_and_large(scale):
+    """Negative scale, zero scale (uniform weights) and scores near 1e3 (no overflow)."""
+    q, k, v, _ = I.prefill_inputs(1, 4, 2, 200, 128, "bf16", seed=13)
+    for causal in (False, True):
+        o, lse = gpu_prefill(q, k, v, causal, scale)
+        ro, rl = oracle.attention(q, k, v, causal, scale)
+        check_bf16(o, ro, f"o scale={scale}")
+        check_close(lse, rl, BF16_LSE_MAX_ABS * max(1.0, abs(scale) * 10), f"lse scale={scale}")
+
+
+def test_bf16_identical_keys_give_prefix_mean():
+    q, k, v, scale = I.prefill_inputs(1, 2, 1, 333, 64, "bf16", seed=17)
+    k = k[:, :, :1].expand(-1, -1, 333, -1).contiguous()
+    o, _ = gpu_prefill(q, k, v, True, scale)
+    means = np.cumsum(f64(v), axis=2) / np.arange(1, 334)[None, None, :, None]
+    err = np.abs(f64(o)[:, :, :, :] - np.repeat(means, 2, axis=1))
+    assert err.max() <= 2e-2
+
+
+def test_bf16_deterministic_and_prefix_invariant():
+    """Two runs are bitwise equal; causal O on the first n rows does not depend on N."""
+    q, k, v, scale = I.prefill_inputs(1, 8, 2, 2048, 128, "bf16", seed=19)
+    o1, l1 = gpu_prefill(q, k, v, True, scale)
+    o2, l2 = gpu_prefill(q, k, v, True, scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    n = 1500
+    o3, l3 = gpu_prefill(q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous(),
+                         True, scale)
+    assert torch.equal(o3, o1[:, :, :n])
+    assert torch.equal(l3, l1[:, :, :n])
+
+
+# ------------------------------------------------------------------ bf16 prefill, full workloads
+def _sampled_check(cfg, heads, rows, all_rows_heads=()):
+    q, k, v, scale = I.prefill_config_inputs(cfg)
+    o, lse = gpu_prefill(q, k, v, cfg.causal, scale)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    ro, rl = oracle.attention_rows(q, k, v, cfg.causal, scale, rows, heads)
+    got = torch.stack([o[b, h, rows] for b, h in heads])
+    got_l = torch.stack([lse[b, h, rows] for b, h in heads])
+    check_bf16(got, ro, f"{cfg.name} sampled o")
+    check_close(got_l, rl, BF16_LSE_MAX_ABS, f"{cfg.name} sampled lse")
+    for b, h in all_rows_heads:
+        allr = np.arange(cfg.N)
+        ro, rl = oracle.attention_rows(q, k, v, cfg.causal, scale, allr, [(b, h)])
+        check_bf16(o[b, h][None], ro, f"{cfg.name} head {(b, h)} all rows")
+        check_close(lse[b, h][None], rl, BF16_LSE_MAX_ABS, f"{cfg.name} head {(b, h)} lse")
+
+
+def test_causal_mha_4k_workload():
+    """B4 H32 N4096 d128 causal bf16: all rows of 2 heads, 70 sampled rows of 12 more."""
+    cfg = I.PREFILL_MHA_4K
+    heads = [(b, h) for b in range(4) for h in (0, 9, 31)]
+    _sampled_check(cfg, heads, I.sample_rows(cfg.N, 48, seed=1), all_rows_heads=[(0, 5), (3, 30)])
+
+
+def test_causal_gqa_16k_workload():
+    """B2 Hq32 Hkv8 N16384 d128 causal bf16: sampled rows over heads of every KV group."""
+    cfg = I.PREFILL_GQA_16K
+    heads = [(0, 0), (0, 5), (1, 14), (1, 31), (0, 23), (1, 8)]
+    _sampled_check(cfg, heads, I.sample_rows(cfg.N, 24, seed=2))
+
+
+def test_causal_gqa_128k_workload():
+    """B1 Hq64 Hkv8 N131072 d128 causal bf16: O(N) memory; sampled rows of 6 heads."""
+    cfg = I.PREFILL_GQA_128K
+    heads = [(0, 0), (0, 7), (0, 8), (0, 33), (0, 62), (0, 63)]
+    rows = [0, 1, 255, 256, 4097, 65535, 65536, 100003, 131070, 131071]
+    _sampled_check(cfg, heads, rows)
+
+
+# ------------------------------------------------------------------ decode
+def test_decode_gqa_workload():
+    """B64 Hq32 Hkv8 d128 bf16, lengths uniform in [1024, 32768], NaN past each length."""
+    cfg = I.DECODE_GQA
+    q, kc, vc, lens, scale = I.decode_config_inputs(cfg)
+    o = gpu_decode(q, kc, vc, lens, scale)
+    ro, _ = oracle.decode(q, kc, vc, lens, scale)
+    check_bf16(o, ro, "decode o")
+    o2 = gpu_decode(q, kc, vc, lens, scale, workspace=True)
+    assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_decode_lengths_and_groups(dtype, d, G):
+    lens = [0, 1, 2, 511, 512, 513, 1024, 1100, 1300, 7]
+    q, kc, vc, ls, scale = I.decode_inputs(len(lens), 2 * G, 2, d, 1, 1300, 1300, dtype, seed=G + d,
+                                           seqlens=lens)
+    o = gpu_decode(q, kc, vc, ls, scale)
+    ro, _ = oracle.decode(q, kc, vc, ls, scale)
+    if dtype == "f32":
+        check_close(o, ro, F32_MAX_ABS, "decode f32")
+    else:
+        check_bf16(o, ro, "decode bf16")
+    assert torch.all(o[0] == 0)  # empty sequence
+
+
+def test_decode_matches_last_prefill_row():
+    """Decode of token i against K,V[0..i] equals causal prefill row i (both on the GPU)."""
+    q, k, v, scale = I.prefill_inputs(2, 8, 2, 700, 128, "bf16", seed=23)
+    o, _ = gpu_prefill(q, k, v, True, scale)
+    for i in (0, 1, 511, 512, 699):
+        lens = torch.full((2,), i + 1, dtype=torch.int32)
+        od = gpu_decode(q[:, :, i].contiguous(), k.contiguous(), v.contiguous(), lens, scale)
+        assert np.abs(f64(od) - f64(o[:, :, i])).max() <= 2e-2

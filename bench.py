@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one fa_prefill call on the causal MHA workload (B4 H32 N4096
+d128 bf16) followed by one fa_decode call on the GQA decode workload (B64
+Hq32 Hkv8 d128 bf16, cache lengths uniform in [1024, 32768]).  Inputs are
+seeded synthetic tensors already resident in HBM before timing starts.
+
+`value` is prefill TFLOP/s (algorithmic FLOPs = 4*d*B*Hq*(N(N+1)/2) over the
+prefill kernel's own HIP-event time); the decode figure (KV bytes read per
+second) is reported beside it.  Kernel durations come from HIP events
+recorded on the stream the kernels are launched on.  A bounded sample of the
+fp64 CPU oracle is timed on the host as a reported baseline.
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc", "prefill_bf16.hip")
+DECODE_SRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc", "decode.hip")
+
+
+def prefill_flops(B, Hq, N, d, causal):
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4 * d * B * Hq * pairs
+
+
+def prefill_bytes(B, Hq, Hkv, N, d, elem=2):
+    return (2 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
+
+
+def decode_bytes(lens, Hq, Hkv, d, elem=2):
+    kv = sum(int(x) for x in lens) * Hkv * d * 2 * elem
+    return kv + 2 * len(lens) * Hq * d * elem + 4 * len(lens)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(name, src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary.
+
+    profiles/<name>.md carries a line `traffic_bytes_per_launch: <int>` and
+    `kernel_source_sha: <hash>`; the figure is only used while the kernel
+    source still has that hash (otherwise null: the counters are stale).
+    """
+    path = os.path.join(PROFILES, name + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != source_hash(src):
+        return None
+    return float(m.group(1))
+
+
+def time_launches(fn, steps, stream):
+    """Run fn() `steps` times; return per-launch event times (ms) and the total."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return per, evs[0].elapsed_time(evs[-1])
+
+
+def cpu_baseline(q, k, v, scale, seconds):
+    """Time the fp64 oracle on sampled causal rows of the prefill workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from exact_tiled_attention_prefill_amd.inputs import sample_rows
+
+    B, Hq, N, d = q.shape
+    rows = sample_rows(N, 64, seed=3)
+    heads = [(b, h) for b in range(B) for h in range(Hq)]
+    done_flops, done_rows, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b, h in heads:
+            oracle.attention_rows(q, k, v, True, scale, rows, [(b, h)])
+            done_flops += sum(4 * d * (r + 1) for r in rows)
+            done_rows += len(rows)
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} causal query rows ({len(rows)} sampled rows x "
+                      f"{done_rows // len(rows)} heads) of the B4 H32 N4096 d128 workload, fp64 numpy, "
+                      f"{dt:.1f} s, 1 BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one kernel only (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); nothing to do for N > 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_tiled_attention_prefill_amd import decode, decode_workspace_bytes, load_library, prefill
+    from exact_tiled_attention_prefill_amd import inputs as I
+
+    load_library()  # fail loudly before any work if libfa.so is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode") and not args.no_decode
+
+    pc = I.PREFILL_MHA_4K
+    if run_prefill:
+        q, k, v, scale = I.prefill_config_inputs(pc)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        od = torch.empty_like(qd)
+        lsed = torch.empty((pc.B, pc.Hq, pc.N), dtype=torch.float32, device=dev)
+
+        def pf():
+            prefill(qd, kd, vd, causal=True, scale=scale, out=od, lse=lsed)
+
+    dc = I.DECODE_GQA
+    if run_decode:
+        dq, dk, dv, dl, dscale = I.decode_config_inputs(dc)
+        lens_host = dl.tolist()
+        dqd, dkd, dvd, dld = dq.to(dev), dk.to(dev), dv.to(dev), dl.to(dev)
+        dod = torch.empty_like(dqd)
+        ws = torch.empty(decode_workspace_bytes(dc.B, dc.Hq, dc.Hkv, dc.maxlen, dc.d), dtype=torch.uint8,
+                         device=dev)
+
+        def df():
+            decode(dqd, dkd, dvd, dld, scale=dscale, out=dod, workspace=ws)
+
+    for _ in range(args.warmup):
+        if run_prefill:
+            pf()
+        if run_decode:
+            df()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each = one prefill + one decode, events per kernel call
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        if run_prefill:
+            pf()
+        ev[i][1].record(stream)
+        if run_decode:
+            df()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
+    d_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
+    p_avg = sum(p_ms) / K
+    d_avg = sum(d_ms) / K
+
+    props = torch.cuda.get_device_properties(dev)
+    result = {
+        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV-read GB/s (% HBM)",
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {"workload": pc.name, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "N": pc.N, "d": pc.d,
+                   "causal": pc.causal, "step": "one prefill (this workload) + one decode (decode.workload)"},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if run_prefill:
+        F = prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True)
+        tflops = F / (p_avg * 1e-3) / 1e12
+        result["value"] = tflops
+        result["prefill"] = {"ms_avg": p_avg, "ms_median": p_ms[K // 2], "ms_min": p_ms[0],
+                             "tflops": tflops, "tokens_per_s": pc.B * pc.N / (p_avg * 1e-3),
+                             "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": F}
+        traffic = measured_traffic("prefill_bf16_mha4k_counters", PREFILL_SRC)
+        result["roofline"] = {"kernel": "prefill_bf16_kernel<128,causal>", "bound": "mfma",
+                              "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                              "algorithmic_bytes": prefill_bytes(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d)}
+    if run_decode:
+        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d)
+        gbs = nbytes / (d_avg * 1e-3) / 1e9
+        result["decode"] = {"workload": dc.name, "ms_avg": d_avg, "ms_median": d_ms[K // 2],
+                            "ms_min": d_ms[0], "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                            "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (d_avg * 1e-3),
+                            "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel",
+                                         "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                         "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC)}}
+        if result["value"] is None:
+            result["value"], result["unit"] = gbs, "GB/s"
+    if run_prefill and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,20 +70,6 @@ def measured_traffic(name, src):
     return float(m.group(1))
 
 
-def time_launches(fn, steps, stream):
-    """Run fn() `steps` times; return per-launch event times (ms) and the total."""
-    import torch
-
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evs[0].record(stream)
-    for i in range(steps):
-        fn()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return per, evs[0].elapsed_time(evs[-1])
-
-
 def cpu_baseline(q, k, v, scale, seconds):
     """Time the fp64 oracle on sampled causal rows of the prefill workload."""
     import numpy as np
@@ -118,8 +104,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run one kernel only (for profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
+                         "copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); nothing to do for N > 1.",
@@ -133,6 +120,14 @@ def main():
 
     load_library()  # fail loudly before any work if libfa.so is missing
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 1 << 30, "launches": args.warmup + args.steps}))
+        return
     stream = torch.cuda.current_stream()
     out = {}
     run_prefill = args.only in (None, "prefill")

@@ -18,9 +18,12 @@
 //     implications for prefill and token generation).
 //
 // gfx950 design:
-//   * Workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//     rows.  Two workgroups share a CU, so every SIMD runs two waves whose
-//     softmax (VALU) and matrix products (MFMA) interleave.  Q stays in VGPRs.
+//   * Workgroup = 4 waves = 128 query rows of one head; two workgroups share
+//     a CU, so every SIMD runs two waves from different workgroups whose
+//     softmax (VALU) and matrix products (MFMA) interleave.  Wave w owns rows
+//     q0 + w + 4j (j = 0..31): interleaving the rows gives every wave the same
+//     causal work, so the per-tile barrier never waits on a wave with more
+//     tiles.  Q stays in VGPRs.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query per
 //     32-key block, so row max and row sum are in-lane plus one
@@ -29,7 +32,12 @@
 //     be permuted freely as long as V^T uses the same order), so P never
 //     touches LDS, and O^T keeps each query's output in its own lane.
 //   * K and V tiles (64 keys) are copied HBM -> LDS by global_load_lds_dwordx4
-//     (no VGPR staging), double-buffered.  K is read with ds_read_b128, V with
+//     (no VGPR staging) into a ring of LDS stages (two by default: the next
+//     tile streams in while the current one is computed; the ring depth, tile
+//     size and waves per workgroup are compile-time parameters -- deeper
+//     rings and 8-wave workgroups were measured slower on MI355X).  The
+//     workgroup barrier between tiles does not drain in-flight DMA.  K is read
+//     with ds_read_b128, V with
 //     the gfx950 transposing ds_read_b64_tr_b16 straight into the MFMA A
 //     operand layout.  16-byte chunks are XOR-swizzled by row so both reads
 //     are bank-conflict free; the DMA source addresses apply the same swizzle.
@@ -49,9 +57,22 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBR = 128;  // query rows per workgroup
-constexpr int kBC = 64;   // keys per tile
+// Launch shape (compile-time): waves per workgroup, keys per tile, ring depth.
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 4
+#endif
+#ifndef FA_PREFILL_BC
+#define FA_PREFILL_BC 64
+#endif
+#ifndef FA_PREFILL_STAGES
+#define FA_PREFILL_STAGES 2
+#endif
+constexpr int kWaves = FA_PREFILL_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;       // query rows per workgroup
+constexpr int kBC = FA_PREFILL_BC;     // keys per tile (32 or 64)
+constexpr int kMB = kBC / 32;          // 32-key MFMA blocks per tile
+constexpr int kStages = FA_PREFILL_STAGES;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // Chunk swizzles (16-byte chunks within a tile row of D/8 chunks).
@@ -66,7 +87,22 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+
+// Workgroup barrier that does not drain the DMA ring.  The caller has
+// already waited (vmcnt) for the tile the next step reads, and every LDS
+// read issued so far has been consumed, so only the s_barrier itself is
+// needed; the empty asm statements keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -76,27 +112,32 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* lds_byte_ptr) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p)));
 }
 
-__device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// One 16-byte-per-lane global -> LDS copy: lane l's 16 bytes from
+// base + off land at lds_wave_base + 16*l.  Written as inline asm so that the
+// compiler does not track it as a pending LDS write (its conservative
+// tracking would otherwise wait for every in-flight ring tile before each LDS
+// read); completion is ordered explicitly by wait_vmem_le() and the ring
+// barrier.  The asm has no register outputs.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int Hq, int Hkv, int N, int n_qtiles, int n_items, float c, uint32_t qflip) {
-  constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
-  constexpr int MD = D / 32;              // 32-row blocks of O^T
-  constexpr int RC = D / 8;               // 16-byte chunks per row
-  constexpr int TILE = kBC * D * 2;       // bytes per K (or V) tile
-  constexpr int CPT = kBC * RC / kThreads;  // DMA chunks per thread per tile
+  constexpr int KS = D / 16;                // k-steps of S^T = K Q^T
+  constexpr int MD = D / 32;                // 32-row blocks of O^T
+  constexpr int RC = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = kBC * D * 2;         // bytes per K (or V) tile
+  constexpr int CPT = kBC * RC / kThreads;  // DMA chunks per thread per K (or V) tile
+  constexpr int DMA_PER_TILE = 2 * CPT;     // vector-memory ops per thread per tile
   static_assert(CPT * kThreads == kBC * RC, "tile must split evenly");
-  // Four distinct LDS objects (K/V x two buffers) so that the compiler can
-  // tell the DMA target of the next tile from the buffer being read.
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE];
+  // Ring of kStages K/V tile pairs.  The DMA into the ring is inline asm, so
+  // the compiler does not track it; ordering is explicit (vmcnt + barrier).
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -122,27 +163,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const uint16_t* kh = k + (size_t)grp * N * D;
   const uint16_t* vh = v + (size_t)grp * N * D;
 
+  // Rows of this wave: q0 + wave + kWaves*j; lane column x holds row q0 + wave + kWaves*x.
   const int q0 = qtile * kBR;
-  const int qw = q0 + wave * 32;
-  const bool wave_has_rows = qw < N;
-  const int wave_last_row = min(qw + 31, N - 1);
+  const int qrow = q0 + wave + kWaves * x;
+  const int wave_first = q0 + wave;
+  const bool wave_has_rows = wave_first < N;
+  const int wave_last_row = min(q0 + wave + kWaves * 31, N - 1);
 
   // Q fragments (B operand of S^T = K Q^T): column x, d = 16ks + 8hi + 0..7.
+  // All loads are issued before any is used (rows past the end read the last
+  // row and are zeroed afterwards).
   bf16x8 qf[KS];
   {
-    const int row = qw + x;
+    const uint16_t* qr = qh + (size_t)min(qrow, N - 1) * D + hi * 8;
+    u32x4 w[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row < N) {
-        w = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + ks * 16 + hi * 8);
-        w ^= qflip;
-      }
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u32x4*>(qr + ks * 16);
+    const uint32_t keep = qrow < N ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (w[ks] ^ qflip) & keep);
   }
 
-  // ---- per-lane LDS read offsets (the tile base and ks/mb/ks2 parts are immediates) ----
+  // ---- per-lane LDS read offsets (tile base and ks/mb/ks2 parts are immediates) ----
   int koff[KS];  // K: row x (+32 mb), chunk (2ks + hi) swizzled
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = x * (D * 2) + (((2 * ks + hi) ^ k_swz<D>(x)) << 4);
@@ -156,25 +198,37 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       voff[md] = row * (D * 2) + (((4 * md + colc) ^ v_swz<D>(row)) << 4) + 8 * (i & 1);
   }
 
-  // ---- DMA: chunk p = i*256 + wave*64 + lane of the tile ----
-  int dma_row[CPT], dma_kc[CPT], dma_vc[CPT];
+  // ---- DMA: chunk p = i*kThreads + wave*64 + lane of the tile; byte offsets within the tile ----
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar: LDS bases go to M0 directly
+  uint32_t dk_off[CPT], dv_off[CPT];
+  int dma_row[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int p = i * kThreads + wave * 64 + lane;
     const int r = p / RC, cp = p % RC;
     dma_row[i] = r;
-    dma_kc[i] = (cp ^ k_swz<D>(r)) * 8;
-    dma_vc[i] = (cp ^ v_swz<D>(r)) * 8;
+    dk_off[i] = (uint32_t)(r * D * 2 + ((cp ^ k_swz<D>(r)) << 4));
+    dv_off[i] = (uint32_t)(r * D * 2 + ((cp ^ v_swz<D>(r)) << 4));
   }
+  // Copy rows [k0, k0+64) of the K and V head slabs into LDS tiles.  Rows past
+  // the end re-read the last row (finite values whose scores are masked).
   auto issue_tile = [&](int t, uint8_t* kl, uint8_t* vl) {
     const int k0 = t * kBC;
-    const bool full = k0 + kBC <= N;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * D * 2;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * D * 2;
+    if (k0 + kBC <= N) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      // rows past the end re-read the last row: finite, and masked out below
-      const int row = full ? k0 + dma_row[i] : min(k0 + dma_row[i], N - 1);
-      dma16(kh + (size_t)row * D + dma_kc[i], kl + (i * kThreads + wave * 64) * 16);
-      dma16(vh + (size_t)row * D + dma_vc[i], vl + (i * kThreads + wave * 64) * 16);
+      for (int i = 0; i < CPT; ++i) {
+        dma16(kbase, dk_off[i], kl + (i * kThreads + wave_s * 64) * 16);
+        dma16(vbase, dv_off[i], vl + (i * kThreads + wave_s * 64) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int delta = (min(dma_row[i], N - 1 - k0) - dma_row[i]) * D * 2;
+        dma16(kbase, dk_off[i] + delta, kl + (i * kThreads + wave_s * 64) * 16);
+        dma16(vbase, dv_off[i] + delta, vl + (i * kThreads + wave_s * 64) * 16);
+      }
     }
   };
 
@@ -186,43 +240,65 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
 
-  issue_tile(0, k_lds0, v_lds0);
-  wait_vmem();
-  __syncthreads();
+  // Wait until tile t+1 has landed: the tiles issued after it (up to
+  // t + kStages - 1, when they exist) may stay in flight.
+  auto wait_next = [&](int t) {
+    const int after = min(kStages - 2, ntiles - 2 - t);
+    static_assert(kStages >= 2 && kStages <= 5, "ring depth");
+    if (kStages >= 5 && after >= 3)
+      wait_vmem_le<3 * DMA_PER_TILE>();
+    else if (kStages >= 4 && after >= 2)
+      wait_vmem_le<2 * DMA_PER_TILE>();
+    else if (kStages >= 3 && after >= 1)
+      wait_vmem_le<DMA_PER_TILE>();
+    else
+      wait_vmem_le<0>();
+  };
 
-  // One tile step: prefetch tile t+1 into (kn, vn) while computing tile t from (kl, vl).
-  auto step = [&](int t, const uint8_t* kl, const uint8_t* vl, uint8_t* kn, uint8_t* vn) {
-    if (t + 1 < ntiles) issue_tile(t + 1, kn, vn);
+  // One tile step: compute tile t from its ring slot while tile t + kStages - 1
+  // streams into the slot freed by tile t - 1.
+  auto step = [&](int t) {
+    if (t + kStages - 1 < ntiles) {
+      const int ns = (t + kStages - 1) % kStages;
+      issue_tile(t + kStages - 1, ring[ns][0], ring[ns][1]);
+    }
+    const uint8_t* kl = ring[t % kStages][0];
+    const uint8_t* vl = ring[t % kStages][1];
     const int k0 = t * kBC;
     const bool active = wave_has_rows && (!CAUSAL || k0 <= wave_last_row);
     if (active) {
       // ---- S^T = K Q^T : s[mb] covers keys 32mb + (8(r/4) + 4hi + r%4), query x ----
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      f32x16 s[kMB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) s[mb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < kMB; ++mb) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[ks] + mb * 32 * D * 2);
           s[mb] = mfma32x32x16(kf, qf[ks], s[mb]);
         }
       // ---- mask: keys past the end, and keys after the query when causal ----
-      if ((k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw)) {
-        const int qrow = qw + x;
+      // key = k0 + 4hi + off(mb,r), off = 32mb + 8(r/4) + r%4: masked when off > lim
+      if ((k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wave_first)) {
+        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool masked = (key >= N) || (CAUSAL && key > qrow);
-            s[mb][r] = masked ? -INFINITY : s[mb][r];
-          }
+          for (int r = 0; r < 16; ++r)
+            s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
       }
       // ---- running softmax (base 2, lazy rescale) ----
-      float mx = -INFINITY;
+      float m4[2 * kMB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int j = 0; j < 2 * kMB; ++j) {
+        const int mb = j >> 1, r0 = 8 * (j & 1);
+        m4[j] = fmaxf(fmaxf(fmaxf(s[mb][r0], s[mb][r0 + 1]), fmaxf(s[mb][r0 + 2], s[mb][r0 + 3])),
+                      fmaxf(fmaxf(s[mb][r0 + 4], s[mb][r0 + 5]), fmaxf(s[mb][r0 + 6], s[mb][r0 + 7])));
+      }
+      float mx = fmaxf(m4[0], m4[1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+      for (int j = 2; j < 2 * kMB; ++j) mx = fmaxf(mx, m4[j]);
       mx = max_halves(mx);
       const float mxs = mx * c;  // -inf stays -inf (c > 0)
       if (__any(mxs > m_run + kTau)) {
@@ -234,16 +310,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         m_run = mn;
       }
       const float negm = -m_run;
-      float lsum = 0.f;
+      float lsum[2] = {0.f, 0.f};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(s[mb][r], c, negm));
           s[mb][r] = p;
-          lsum += p;
+          lsum[r & 1] += p;
         }
-      l_run += lsum;
+      l_run += lsum[0] + lsum[1];
       // ---- O^T += V^T P^T over four 16-key steps ----
 #pragma unroll
       for (int ks2 = 0; ks2 < kBC / 16; ++ks2) {
@@ -260,21 +336,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         }
       }
     }
-    wait_vmem();
-    __syncthreads();
+    if (t + 1 < ntiles) wait_next(t);
+    ring_barrier();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (t + 1 < ntiles) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+
+  // prologue: tiles 0 .. kStages-2 in flight; wait for tile 0
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) issue_tile(t, ring[t][0], ring[t][1]);
+  {
+    const int after = min(kStages - 2, ntiles - 1);
+    if (kStages >= 5 && after >= 3)
+      wait_vmem_le<3 * DMA_PER_TILE>();
+    else if (kStages >= 4 && after >= 2)
+      wait_vmem_le<2 * DMA_PER_TILE>();
+    else if (kStages >= 3 && after >= 1)
+      wait_vmem_le<DMA_PER_TILE>();
+    else
+      wait_vmem_le<0>();
   }
+  ring_barrier();
+  for (int t = 0; t < ntiles; ++t) step(t);
 
   // ---- epilogue: O = O^T / l, lse = m ln2 + ln l ----
   if (!wave_has_rows) return;
   const float lt = sum_halves(l_run);
   const float inv = 1.0f / lt;
-  const int row = qw + x;
-  if (row < N) {
-    uint16_t* orow = o + qbase + (size_t)row * D;
+  if (qrow < N) {
+    uint16_t* orow = o + qbase + (size_t)qrow * D;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -284,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                    pack_bf16x2(oacc[md][4 * g4 + 2] * inv, oacc[md][4 * g4 + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-    if (lse != nullptr && hi == 0) lse[(size_t)bh * N + row] = m_run * kLn2 + __logf(lt);
+    if (lse != nullptr && hi == 0) lse[(size_t)bh * N + qrow] = m_run * kLn2 + __logf(lt);
   }
 }
 

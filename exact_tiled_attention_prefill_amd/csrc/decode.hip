@@ -10,13 +10,22 @@
 //
 // Split-KV design for gfx950:
 //   kernel 1 (split): one workgroup per (sequence, key/value head, query-head
-//     slice, 512-key chunk).  Every K/V byte of the chunk is read from HBM
+//     slice, chunk of keys).  Every K/V byte of the chunk is read from HBM
 //     exactly once and used for all query heads of the GQA group ("Optimizing
 //     memory requirements for inference in large language models", GQA
-//     paragraph).  Scores: 4 lanes per cache row (64 contiguous bytes each),
-//     all loads of a pass issued before use; values: 16 lanes per row.  The
-//     chunk's softmax statistics are reduced in-wave and across waves in
-//     LDS.  Output per chunk: its normalised partial o_s and its log-sum-exp.
+//     paragraph).  Output per chunk: its normalised partial o_s and its
+//     log-sum-exp.
+//     bf16 path (1024-key chunks): the chunk streams through a 4-stage ring of
+//       32-key K/V tiles copied HBM -> LDS by global_load_lds_dwordx4, three
+//       tiles ahead of compute, so many bytes are in flight per CU with no
+//       VGPR staging.  Scores use 8 lanes per key and v_dot2_f32_bf16 (two
+//       bf16 products per instruction, no widening); values are read with the
+//       transposing ds_read_b64_tr_b16 so each lane owns fixed output columns
+//       and accumulates pairs of keys with v_dot2_f32_bf16 against bf16
+//       probabilities.  Each wave keeps its own running max / sum (lazy
+//       rescale); the four waves are merged once per chunk through LDS.
+//     fp32 path (512-key chunks): plain VGPR loads and fp32 FMAs, 4 lanes per
+//       row for scores and 16 (or 32) lanes per row for values.
 //   kernel 2 (combine): per (sequence, query head), the partials are merged
 //     with weights exp(lse_s - max lse) -- the running-softmax rule applied to
 //     whole chunks ("11.4d FlashAttention", "Online Softmax").
@@ -284,11 +293,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 template <typename T, int D>
 __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seqlens, T* __restrict__ o, int Hq, int maxlen, int nsplit) {
+    const int32_t* __restrict__ seqlens, T* __restrict__ o, int Hq, int maxlen, int nsplit, int chunk) {
   using E = Elem<T>;
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = min(max(seqlens[b], 0), maxlen);
-  const int ns = (L + kChunk - 1) / kChunk;
+  const int ns = (L + chunk - 1) / chunk;
   const size_t base = ((size_t)b * Hq + h) * nsplit;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float out = 0.f;
@@ -307,6 +316,310 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 split kernel: DMA ring + dot2.
+constexpr int kChunkB = 1024;   // keys per workgroup
+constexpr int kStageKeys = 32;  // keys per ring stage
+constexpr int kRingB = 4;       // ring stages (three in flight ahead of compute)
+constexpr float kTauB = 8.0f;   // lazy-rescale threshold (log2 units)
+
+template <int n>
+__device__ __forceinline__ void dec_wait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+__device__ __forceinline__ void dec_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// lane l's 16 bytes from base + off land at lds_wave_base + 16*l (inline asm:
+// the compiler does not track it; completion is ordered by vmcnt + barrier)
+__device__ __forceinline__ void dec_dma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
+}
+typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) dec_i16x4 lds_t;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(p)));
+}
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float a) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), CTRL, 0xF, 0xF, false));
+}
+
+// grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
+template <int D, int GT>
+__global__ __launch_bounds__(256, 2) void decode_bf16_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int Hq, int Hkv, int maxlen, int nsplit, float c, uint32_t qflip) {
+  constexpr int RC = D / 8;                         // 16-byte chunks per cache row
+  constexpr int STAGE = kStageKeys * D * 2;         // bytes per K (or V) stage
+  constexpr int CPT = kStageKeys * RC / 256;        // DMA chunks per thread per K (or V) stage
+  constexpr int DMA_PER_STAGE = 2 * CPT;
+  constexpr int EPL = D / 8;                        // score phase: elements per lane (8 lanes/key)
+  constexpr int NCB = D / 64;                       // value phase: 64-column blocks
+  static_assert(CPT >= 1 && CPT * 256 == kStageKeys * RC, "stage must split evenly");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingB][2][STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][GT][8];
+  __shared__ float m_w[4][GT], l_w[4][GT];
+  static_assert(4 * GT * D * 4 <= kRingB * 2 * STAGE, "wave partials must fit in the ring");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int split = blockIdx.x;
+  const int G = Hq / Hkv;
+  const int slices = G / GT;
+  const int kvh = blockIdx.y / slices;
+  const int h0 = kvh * G + (blockIdx.y % slices) * GT;
+  const int b = blockIdx.z;
+
+  const int L = min(max(seqlens[b], 0), maxlen);
+  const int kbeg = split * kChunkB;
+  if (kbeg >= L) return;
+  const int n = min(kChunkB, L - kbeg);
+  const int nst = (n + kStageKeys - 1) / kStageKeys;
+  const size_t cbase = (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(kc + cbase);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(vc + cbase);
+
+  // ---- score layout: key kk = lane/8 of the wave's 8 keys, part j = lane%8 (EPL elements) ----
+  const int kk = lane >> 3;
+  const int j = lane & 7;
+  uint32_t qv[GT][EPL / 2];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(q + ((size_t)b * Hq + h0 + g) * D + j * EPL);
+#pragma unroll
+    for (int e = 0; e < EPL / 2; e += 4) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qr + e);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qv[g][e + t] = w[t] ^ qflip;
+    }
+  }
+  // K LDS reads: row 8*wave + kk, logical chunks j*EPL/8 .. (row-major, chunk ^ (row & 1) for D=128)
+  const int krow = 8 * wave + kk;
+  int kofs[EPL / 8];
+#pragma unroll
+  for (int e = 0; e < EPL / 8; ++e) {
+    const int ch = j * (EPL / 8) + e;
+    kofs[e] = krow * D * 2 + ((D == 128 ? (ch ^ (krow & 1)) : ch) << 4);
+  }
+  // V transposing reads: lane i of 16-lane group gm reads row 8*wave + 4kq + (i>>2),
+  // columns 64cb + 16gm + 4(i&3) .. +3; it receives column 64cb + lane for 4 keys.
+  int vofs[NCB];
+  {
+    const int i = lane & 15, gm = lane >> 4;
+    const int vrow = 8 * wave + (i >> 2);
+    const int vsw = D == 128 ? 4 * (vrow & 3) : 4 * ((vrow >> 1) & 1);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int ch = (64 * cb + 16 * gm + 4 * (i & 3)) >> 3;
+      vofs[cb] = vrow * D * 2 + ((ch ^ vsw) << 4) + 8 * (i & 1);
+    }
+  }
+  // DMA: chunk p = i*256 + tid of a stage: row p / RC, chunk p % RC (swizzled like the reads)
+  uint32_t dk[CPT], dv[CPT];
+  int drow[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int p = i * 256 + tid;
+    const int r = p / RC, cp = p % RC;
+    drow[i] = r;
+    const int ksw = D == 128 ? (cp ^ (r & 1)) : cp;
+    const int vsw = D == 128 ? (cp ^ (4 * (r & 3))) : (cp ^ (4 * ((r >> 1) & 1)));
+    dk[i] = (uint32_t)(r * D * 2 + (ksw << 4));
+    dv[i] = (uint32_t)(r * D * 2 + (vsw << 4));
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int st) {
+    const int r0 = st * kStageKeys;
+    const uint8_t* kb = kp + (size_t)r0 * D * 2;
+    const uint8_t* vb = vp + (size_t)r0 * D * 2;
+    uint8_t* kl = ring[st % kRingB][0];
+    uint8_t* vl = ring[st % kRingB][1];
+    if (r0 + kStageKeys <= n) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        dec_dma16(kb, dk[i], kl + (i * 256 + wave_s * 64) * 16);
+        dec_dma16(vb, dv[i], vl + (i * 256 + wave_s * 64) * 16);
+      }
+    } else {
+      // rows past the sequence end re-read its last row (never past it: the
+      // cache there may hold anything); their scores are masked below
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int delta = (min(drow[i], n - 1 - r0) - drow[i]) * D * 2;
+        dec_dma16(kb, dk[i] + delta, kl + (i * 256 + wave_s * 64) * 16);
+        dec_dma16(vb, dv[i] + delta, vl + (i * 256 + wave_s * 64) * 16);
+      }
+    }
+  };
+  auto wait_stage = [&](int st) {  // stage st landed; later ones may be in flight
+    const int after = min(kRingB - 2, nst - 1 - st);
+    if (after >= 2)
+      dec_wait_vmem_le<2 * DMA_PER_STAGE>();
+    else if (after == 1)
+      dec_wait_vmem_le<DMA_PER_STAGE>();
+    else
+      dec_wait_vmem_le<0>();
+  };
+
+  float m_run[GT], l_part[GT], oacc[GT][NCB];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m_run[g] = -INFINITY;
+    l_part[g] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] = 0.f;
+  }
+
+#pragma unroll
+  for (int st = 0; st < kRingB - 1; ++st)
+    if (st < nst) issue(st);
+  wait_stage(0);
+  dec_barrier();
+
+  for (int st = 0; st < nst; ++st) {
+    if (st + kRingB - 1 < nst) issue(st + kRingB - 1);
+    const uint8_t* kl = ring[st % kRingB][0];
+    const uint8_t* vl = ring[st % kRingB][1];
+    // ---- scores of this wave's 8 keys for GT heads ----
+    uint32_t kw[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 8; ++e) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kl + kofs[e]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kw[4 * e + t] = w[t];
+    }
+    const bool valid = st * kStageKeys + krow < n;
+    float sc[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) a = dot2bf(kw[e], qv[g][e], a);
+      a += dpp_f<0xB1>(a);   // quad_perm [1,0,3,2]
+      a += dpp_f<0x4E>(a);   // quad_perm [2,3,0,1]
+      a += dpp_f<0x141>(a);  // row_half_mirror: joins the two quads of the 8 lanes
+      sc[g] = valid ? a * c : -INFINITY;
+    }
+    // ---- running max over the wave's keys (lazy rescale) ----
+    float mx[GT];
+    bool grow = false;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float t = fmaxf(sc[g], dpp_f<0x128>(sc[g]));  // row_ror:8 -> other key of the 16-lane row
+      t = fmaxf(t, __shfl_xor(t, 16, 64));
+      mx[g] = max_halves(t);
+      grow = grow || (mx[g] > m_run[g] + kTauB);
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float mn = fmaxf(m_run[g], mx[g]);
+        const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m_run[g] - mn);
+        l_part[g] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] *= alpha;
+        m_run[g] = mn;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float negm = (m_run[g] == -INFINITY) ? 0.f : -m_run[g];
+      const float p = fast_exp2(sc[g] + negm);
+      if (j == 0) {
+        l_part[g] += p;
+        p_lds[wave][g][kk] = (uint16_t)(pack_bf16x2(p, 0.f) & 0xffffu);
+      }
+    }
+    // ---- values: each lane owns columns 64cb + lane ----
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const u32x4 pp = *reinterpret_cast<const u32x4*>(&p_lds[wave][g][0]);
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const u32x2 vq = dec_read_tr(vl + vofs[cb] + 4 * kq * D * 2);
+          oacc[g][cb] = dot2bf(vq[0], pp[2 * kq], oacc[g][cb]);
+          oacc[g][cb] = dot2bf(vq[1], pp[2 * kq + 1], oacc[g][cb]);
+        }
+    }
+    if (st + 1 < nst) wait_stage(st + 1);
+    dec_barrier();
+  }
+
+  // ---- merge the four waves' (m, l, o); the ring is idle now (every DMA was
+  // waited for and every wave passed the last barrier), so it holds o ----
+  float(&o_w)[4][GT][D] = *reinterpret_cast<float(*)[4][GT][D]>(&ring[0][0][0]);
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    float s = l_part[g];
+    s += __shfl_xor(s, 8, 64);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);  // lanes j == 0 held the per-key sums
+    if (lane == 0) {
+      m_w[wave][g] = m_run[g];
+      l_w[wave][g] = s;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o_w[wave][g][64 * cb + lane] = oacc[g][cb];
+  }
+  __syncthreads();
+  for (int i = tid; i < GT * D; i += 256) {
+    const int g = i / D, d = i % D;
+    float M = m_w[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, m_w[w][g]);
+    float l = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(m_w[w][g] - M);  // 0 for a wave that saw no key
+      l = fmaf(l_w[w][g], f, l);
+      a = fmaf(o_w[w][g][d], f, a);
+    }
+    const size_t pidx = ((size_t)b * Hq + h0 + g) * nsplit + split;
+    part_o[pidx * D + d] = a / l;
+    if (d == 0) part_lse[pidx] = M * kLn2 + __logf(l);
+  }
+}
+
+template <int D, int GT>
+hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
+  const int nsplit = (a.maxlen + kChunkB - 1) / kChunkB;
+  const int G = a.Hq / a.Hkv;
+  float* part_o = static_cast<float*>(a.ws);
+  const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
+  dim3 g1(nsplit, a.Hkv * (G / GT), a.B);
+  if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_bf16_split_kernel<D, GT>), g1, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
+                     nsplit, a.c, a.neg ? 0x80008000u : 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(128), 0, stream, part_o,
+                     part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, kChunkB);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (G % 8 == 0) return launch_bf16<D, 8>(a, stream);
+  if (G % 4 == 0) return launch_bf16<D, 4>(a, stream);
+  if (G % 2 == 0) return launch_bf16<D, 2>(a, stream);
+  return launch_bf16<D, 1>(a, stream);
+}
+
 template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int nsplit = (a.maxlen + kChunk - 1) / kChunk;
@@ -322,7 +635,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(128), 0, stream, part_o, part_lse,
-                     a.seqlens, static_cast<T*>(a.o), a.Hq, a.maxlen, nsplit);
+                     a.seqlens, static_cast<T*>(a.o), a.Hq, a.maxlen, nsplit, kChunk);
   return hipGetLastError();
 }
 
@@ -344,8 +657,8 @@ size_t decode_workspace_bytes(int B, int Hq, int maxlen, int d) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_g<uint16_t, 128>(a, stream);
-  if (a.d == 64) return launch_g<uint16_t, 64>(a, stream);
+  if (a.d == 128) return launch_bf16_g<128>(a, stream);
+  if (a.d == 64) return launch_bf16_g<64>(a, stream);
   return hipErrorInvalidValue;
 }
 

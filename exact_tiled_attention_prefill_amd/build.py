@@ -29,8 +29,11 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code: hipcc would
 # otherwise emit v_pk_{add,mul,fma}_f32 from ordinary float code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The kernels reinterpret LDS and register data between element types (bf16
+# pairs, 16-byte vectors); strict-aliasing based reordering is turned off so
+# such accesses keep their program order.
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-                "-Wno-unused-function", "-I", INCLUDE] + DEVICE_FLAGS
+                "-Wno-unused-function", "-fno-strict-aliasing", "-I", INCLUDE] + DEVICE_FLAGS
 
 
 def hipcc():

@@ -15,10 +15,12 @@
 //     memory requirements for inference in large language models", GQA
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
-//     bf16 path (1024-key chunks): the chunk streams through a 4-stage ring of
-//       32-key K/V tiles copied HBM -> LDS by global_load_lds_dwordx4, three
-//       tiles ahead of compute, so many bytes are in flight per CU with no
-//       VGPR staging.  Scores use 8 lanes per key and v_dot2_f32_bf16 (two
+//     bf16 path (512-key chunks): the chunk streams through a ring of 32-key
+//       K/V tiles copied HBM -> LDS by global_load_lds_dwordx4 (no VGPR
+//       staging).  The ring is only two stages deep so that four workgroups
+//       (16 waves) fit per CU: on MI355X the number of resident workgroups
+//       hides the per-tile dependency chain better than a deeper ring does
+//       (chunk size, ring depth and blocks per CU are compile-time knobs).  Scores use 8 lanes per key and v_dot2_f32_bf16 (two
 //       bf16 products per instruction, no widening); values are read with the
 //       transposing ds_read_b64_tr_b16 so each lane owns fixed output columns
 //       and accumulates pairs of keys with v_dot2_f32_bf16 against bf16
@@ -40,6 +42,15 @@ namespace {
 constexpr int kChunk = kDecodeChunk;  // keys per split
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = kChunk / kWaves;  // 128
+
+// Bytes of the split-KV partials ([B,Hq,nsplit,d] fp32 outputs, then
+// [B,Hq,nsplit] fp32 log-sum-exps, each padded to 256 bytes) for a chunk size.
+size_t partials_bytes(int B, int Hq, int maxlen, int d, int chunk) {
+  const size_t nsplit = ((size_t)maxlen + chunk - 1) / chunk;
+  const size_t po = (size_t)B * Hq * nsplit * d * sizeof(float);
+  const size_t pl = (size_t)B * Hq * nsplit * sizeof(float);
+  return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
+}
 
 template <typename T>
 struct Elem;
@@ -318,9 +329,22 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
 
 // ---------------------------------------------------------------------------
 // bf16 split kernel: DMA ring + dot2.
-constexpr int kChunkB = 1024;   // keys per workgroup
-constexpr int kStageKeys = 32;  // keys per ring stage
-constexpr int kRingB = 4;       // ring stages (three in flight ahead of compute)
+#ifndef FA_DEC_CHUNK
+#define FA_DEC_CHUNK 512
+#endif
+#ifndef FA_DEC_PASSES
+#define FA_DEC_PASSES 1
+#endif
+#ifndef FA_DEC_RING
+#define FA_DEC_RING 2
+#endif
+#ifndef FA_DEC_MINBLOCKS
+#define FA_DEC_MINBLOCKS 4
+#endif
+constexpr int kChunkB = FA_DEC_CHUNK;            // keys per workgroup
+constexpr int kPasses = FA_DEC_PASSES;           // 32-key passes per ring stage
+constexpr int kStageKeys = 32 * kPasses;         // keys per ring stage
+constexpr int kRingB = FA_DEC_RING;              // ring stages (kRingB - 1 in flight ahead of compute)
 constexpr float kTauB = 8.0f;   // lazy-rescale threshold (log2 units)
 
 template <int n>
@@ -343,6 +367,14 @@ __device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
   typedef __attribute__((address_space(3))) dec_i16x4 lds_t;
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(p)));
 }
+// Order LDS traffic between lanes of one wave: data written by some lanes is
+// read by others (and later overwritten), which without this is a data race
+// the compiler may exploit (e.g. by sinking the read into the writers' branch).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
@@ -353,7 +385,7 @@ __device__ __forceinline__ float dpp_f(float a) {
 
 // grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
 template <int D, int GT>
-__global__ __launch_bounds__(256, 2) void decode_bf16_split_kernel(
+__global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
     int Hq, int Hkv, int maxlen, int nsplit, float c, uint32_t qflip) {
@@ -462,9 +494,14 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_split_kernel(
   };
   auto wait_stage = [&](int st) {  // stage st landed; later ones may be in flight
     const int after = min(kRingB - 2, nst - 1 - st);
-    if (after >= 2)
+    static_assert(kRingB >= 2 && kRingB <= 6, "ring depth");
+    if (kRingB >= 6 && after >= 4)
+      dec_wait_vmem_le<4 * DMA_PER_STAGE>();
+    else if (kRingB >= 5 && after >= 3)
+      dec_wait_vmem_le<3 * DMA_PER_STAGE>();
+    else if (kRingB >= 4 && after >= 2)
       dec_wait_vmem_le<2 * DMA_PER_STAGE>();
-    else if (after == 1)
+    else if (kRingB >= 3 && after >= 1)
       dec_wait_vmem_le<DMA_PER_STAGE>();
     else
       dec_wait_vmem_le<0>();
@@ -489,68 +526,78 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_split_kernel(
     if (st + kRingB - 1 < nst) issue(st + kRingB - 1);
     const uint8_t* kl = ring[st % kRingB][0];
     const uint8_t* vl = ring[st % kRingB][1];
-    // ---- scores of this wave's 8 keys for GT heads ----
-    uint32_t kw[EPL / 2];
 #pragma unroll
-    for (int e = 0; e < EPL / 8; ++e) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kl + kofs[e]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kw[4 * e + t] = w[t];
-    }
-    const bool valid = st * kStageKeys + krow < n;
-    float sc[GT];
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL / 2; ++e) a = dot2bf(kw[e], qv[g][e], a);
-      a += dpp_f<0xB1>(a);   // quad_perm [1,0,3,2]
-      a += dpp_f<0x4E>(a);   // quad_perm [2,3,0,1]
-      a += dpp_f<0x141>(a);  // row_half_mirror: joins the two quads of the 8 lanes
-      sc[g] = valid ? a * c : -INFINITY;
-    }
-    // ---- running max over the wave's keys (lazy rescale) ----
-    float mx[GT];
-    bool grow = false;
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float t = fmaxf(sc[g], dpp_f<0x128>(sc[g]));  // row_ror:8 -> other key of the 16-lane row
-      t = fmaxf(t, __shfl_xor(t, 16, 64));
-      mx[g] = max_halves(t);
-      grow = grow || (mx[g] > m_run[g] + kTauB);
-    }
-    if (__any(grow)) {
-#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      // ---- scores of this wave's 8 keys for GT heads ----
+      uint32_t kw[EPL / 2];
+  #pragma unroll
+      for (int e = 0; e < EPL / 8; ++e) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(kl + kofs[e] + 32 * pass * D * 2);
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) kw[4 * e + t] = w[t];
+      }
+      const bool valid = st * kStageKeys + 32 * pass + krow < n;
+      float sc[GT];
+  #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        const float mn = fmaxf(m_run[g], mx[g]);
-        const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m_run[g] - mn);
-        l_part[g] *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] *= alpha;
-        m_run[g] = mn;
+        float a = 0.f;
+  #pragma unroll
+        for (int e = 0; e < EPL / 2; ++e) a = dot2bf(kw[e], qv[g][e], a);
+        a += dpp_f<0xB1>(a);   // quad_perm [1,0,3,2]
+        a += dpp_f<0x4E>(a);   // quad_perm [2,3,0,1]
+        a += dpp_f<0x141>(a);  // row_half_mirror: joins the two quads of the 8 lanes
+        sc[g] = valid ? a * c : -INFINITY;
       }
-    }
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float negm = (m_run[g] == -INFINITY) ? 0.f : -m_run[g];
-      const float p = fast_exp2(sc[g] + negm);
-      if (j == 0) {
-        l_part[g] += p;
-        p_lds[wave][g][kk] = (uint16_t)(pack_bf16x2(p, 0.f) & 0xffffu);
+      // ---- running max over the wave's keys (lazy rescale) ----
+      float mx[GT];
+      bool grow = false;
+  #pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float t = fmaxf(sc[g], dpp_f<0x128>(sc[g]));  // row_ror:8 -> other key of the 16-lane row
+        {
+        // v_permlane16_swap: one result holds the even 16-lane row's value and
+        // the other the odd row's, in every lane of the pair of rows
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+        t = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
       }
-    }
-    // ---- values: each lane owns columns 64cb + lane ----
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const u32x4 pp = *reinterpret_cast<const u32x4*>(&p_lds[wave][g][0]);
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const u32x2 vq = dec_read_tr(vl + vofs[cb] + 4 * kq * D * 2);
-          oacc[g][cb] = dot2bf(vq[0], pp[2 * kq], oacc[g][cb]);
-          oacc[g][cb] = dot2bf(vq[1], pp[2 * kq + 1], oacc[g][cb]);
+        mx[g] = max_halves(t);
+        grow = grow || (mx[g] > m_run[g] + kTauB);
+      }
+      if (__any(grow)) {
+  #pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const float mn = fmaxf(m_run[g], mx[g]);
+          const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m_run[g] - mn);
+          l_part[g] *= alpha;
+  #pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] *= alpha;
+          m_run[g] = mn;
         }
+      }
+  #pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float negm = (m_run[g] == -INFINITY) ? 0.f : -m_run[g];
+        const float p = fast_exp2(sc[g] + negm);
+        if (j == 0) {
+          l_part[g] += p;
+          p_lds[wave][g][kk] = (uint16_t)(pack_bf16x2(p, 0.f) & 0xffffu);
+        }
+      }
+      wave_sync();  // p_lds written by the lanes j == 0, read by every lane
+      // ---- values: each lane owns columns 64cb + lane ----
+  #pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const u32x4 pp = *reinterpret_cast<const u32x4*>(&p_lds[wave][g][0]);
+  #pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+  #pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const u32x2 vq = dec_read_tr(vl + vofs[cb] + (32 * pass + 4 * kq) * D * 2);
+            oacc[g][cb] = dot2bf(vq[0], pp[2 * kq], oacc[g][cb]);
+            oacc[g][cb] = dot2bf(vq[1], pp[2 * kq + 1], oacc[g][cb]);
+          }
+      }
+      wave_sync();  // every lane has read p_lds before the next pass rewrites it
     }
     if (st + 1 < nst) wait_stage(st + 1);
     dec_barrier();
@@ -593,6 +640,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_split_kernel(
 
 template <int D, int GT>
 hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, kChunkB) > a.ws_bytes) return hipErrorInvalidValue;
   const int nsplit = (a.maxlen + kChunkB - 1) / kChunkB;
   const int G = a.Hq / a.Hkv;
   float* part_o = static_cast<float*>(a.ws);
@@ -622,6 +670,7 @@ hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, kChunk) > a.ws_bytes) return hipErrorInvalidValue;
   const int nsplit = (a.maxlen + kChunk - 1) / kChunk;
   const int G = a.Hq / a.Hkv;
   float* part_o = static_cast<float*>(a.ws);
@@ -650,10 +699,10 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Hq, int maxlen, int d) {
-  const size_t nsplit = ((size_t)maxlen + kChunk - 1) / kChunk;
-  const size_t po = (size_t)B * Hq * nsplit * d * sizeof(float);
-  const size_t pl = (size_t)B * Hq * nsplit * sizeof(float);
-  return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
+  // large enough for either path's chunking
+  const size_t a = partials_bytes(B, Hq, maxlen, d, kChunk);
+  const size_t b = partials_bytes(B, Hq, maxlen, d, kChunkB);
+  return a > b ? a : b;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {

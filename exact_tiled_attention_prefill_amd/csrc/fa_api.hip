@@ -101,7 +101,8 @@ int decode_run(const void* q, const void* kc, const void* vc, const int32_t* seq
     }
     owned = true;
   }
-  fa::DecodeArgs a{q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, softmax_coeff(scale), scale < 0.f, ws};
+  fa::DecodeArgs a{q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, softmax_coeff(scale), scale < 0.f, ws,
+                   owned ? need : ws_bytes};
   hipError_t e = bf16 ? fa::launch_decode_bf16(a, s) : fa::launch_decode_f32(a, s);
   if (owned) {
     hipError_t f = hipFreeAsync(ws, s);

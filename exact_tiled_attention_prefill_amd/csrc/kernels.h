@@ -36,7 +36,8 @@ struct DecodeArgs {
   int B, Hq, Hkv, maxlen, d;
   float c;
   bool neg;
-  void* ws;  // >= decode_workspace_bytes(...)
+  void* ws;        // >= decode_workspace_bytes(...)
+  size_t ws_bytes; // size of ws; each launch checks its own partial layout fits
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

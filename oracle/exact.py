@@ -10,8 +10,8 @@ section):
   score matrix between them, re-reading the whole KV cache (plus the newest
   entry) when one new token is generated.  -- forum comment on SRAM and GEMM
   tiling (item 45450456), the paragraph on KV caching.
-* The tiled method is exact: it yields the standard attention result,
-  attention.  -- "11.4d FlashAttention", comparison table in "How
+* The tiled method is exact: it yields the standard attention result.
+  -- "11.4d FlashAttention", comparison table in "How
   FlashAttention Fixes This"; "How Does Flash Attention Reduce Memory Traffic
   During Local Inference?", section "Flash Attention Tiles the Problem Into
   On-Chip Working Sets".

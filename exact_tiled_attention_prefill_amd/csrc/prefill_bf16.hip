@@ -278,6 +278,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[ks] + mb * 32 * D * 2);
           s[mb] = mfma32x32x16(kf, qf[ks], s[mb]);
         }
+      // let the scheduler interleave the K fragment reads with the MFMAs
+      __builtin_amdgcn_iglp_opt(0);
       // ---- mask: keys past the end, and keys after the query when causal ----
       // key = k0 + 4hi + off(mb,r), off = 32mb + 8(r/4) + r%4: masked when off > lim
       if ((k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wave_first)) {
@@ -289,17 +291,19 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
             s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
       }
       // ---- running softmax (base 2, lazy rescale) ----
-      float m4[2 * kMB];
+      // four independent chains of three-input maxima over the lane's scores
+      float m4[4];
 #pragma unroll
-      for (int j = 0; j < 2 * kMB; ++j) {
-        const int mb = j >> 1, r0 = 8 * (j & 1);
-        m4[j] = fmaxf(fmaxf(fmaxf(s[mb][r0], s[mb][r0 + 1]), fmaxf(s[mb][r0 + 2], s[mb][r0 + 3])),
-                      fmaxf(fmaxf(s[mb][r0 + 4], s[mb][r0 + 5]), fmaxf(s[mb][r0 + 6], s[mb][r0 + 7])));
+      for (int j = 0; j < 4; ++j) {
+        constexpr int per = 16 * kMB / 4;  // scores per chain
+        const int e0 = j * per;
+        float m = fmaxf(s[e0 >> 4][e0 & 15], s[(e0 + 1) >> 4][(e0 + 1) & 15]);
+#pragma unroll
+        for (int e = e0 + 2; e + 1 < e0 + per; e += 2)
+          m = fmaxf(fmaxf(m, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
+        m4[j] = m;
       }
-      float mx = fmaxf(m4[0], m4[1]);
-#pragma unroll
-      for (int j = 2; j < 2 * kMB; ++j) mx = fmaxf(mx, m4[j]);
-      mx = max_halves(mx);
+      float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
       const float mxs = mx * c;  // -inf stays -inf (c > 0)
       if (__any(mxs > m_run + kTau)) {
         const float mn = fmaxf(m_run, mxs);
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
         }
       }
     }
+    __builtin_amdgcn_iglp_opt(0);
     if (t + 1 < ntiles) wait_next(t);
     ring_barrier();
   };

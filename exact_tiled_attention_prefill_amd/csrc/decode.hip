@@ -52,6 +52,18 @@ size_t partials_bytes(int B, int Hq, int maxlen, int d, int chunk) {
   return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
 }
 
+// Chunk handled by this workgroup.  Workgroups go to the 8 XCDs round-robin
+// by linear id, with x (the split) fastest, and only a prefix of each
+// (sequence, head) row's splits has keys -- a prefix whose length varies by
+// sequence.  Without a rotation, split s of every row lands on XCD s % 8 when
+// the split count is a multiple of 8, so the low XCDs get every row's odd
+// remainder (about 10% more work than the average for uniform random
+// lengths); rotating each row's chunk order by its row index spreads them.
+__device__ __forceinline__ int split_of_block(int nsplit) {
+  const int row = blockIdx.y + gridDim.y * blockIdx.z;
+  return (nsplit & 7) == 0 ? (int)((blockIdx.x + (unsigned)row) % (unsigned)nsplit) : (int)blockIdx.x;
+}
+
 template <typename T>
 struct Elem;
 template <>
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int split = blockIdx.x;
+  const int split = split_of_block(nsplit);
   const int G = Hq / Hkv;
   const int slices = G / GT;
   const int kvh = blockIdx.y / slices;
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kerne
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int split = blockIdx.x;
+  const int split = split_of_block(nsplit);
   const int G = Hq / Hkv;
   const int slices = G / GT;
   const int kvh = blockIdx.y / slices;

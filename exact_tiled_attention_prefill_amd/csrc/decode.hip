@@ -312,30 +312,89 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-// grid: x = query head, y = sequence; block = D threads.
+// grid: x = query head, y = sequence; block = 256 threads.
+// The chunk partials of one (sequence, query head) are merged with weights
+// exp(lse_s - max lse).  All loads are independent of one another: the max
+// is a strided block reduction, the weights go through LDS in batches, and
+// thread group sg (256 / D groups of D threads, one column each) accumulates
+// splits sg, sg + 256/D, ... with unrolled, coalesced row loads.
+constexpr int kCombThreads = 256;
+constexpr int kCombBatch = 1024;  // weights staged in LDS per batch
+
 template <typename T, int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ seqlens, T* __restrict__ o, int Hq, int maxlen, int nsplit, int chunk) {
   using E = Elem<T>;
+  constexpr int NG = kCombThreads / D;  // split groups
+  __shared__ float w_lds[kCombBatch];
+  __shared__ float red[kCombThreads / 64];
+  __shared__ float acc_lds[NG][D];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = min(max(seqlens[b], 0), maxlen);
   const int ns = (L + chunk - 1) / chunk;
+  T* orow = o + ((size_t)b * Hq + h) * D;
+  if (ns == 0) {
+    if (tid < D) E::store1(orow + tid, 0.f);
+    return;
+  }
   const size_t base = ((size_t)b * Hq + h) * nsplit;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float out = 0.f;
-    if (ns > 0) {
-      float mx = -INFINITY;
-      for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[base + s]);
-      float wsum = 0.f, acc = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float w = __expf(part_lse[base + s] - mx);
-        wsum += w;
-        acc = fmaf(w, part_o[(base + s) * D + d], acc);
-      }
-      out = acc / wsum;
+  const float* lse = part_lse + base;
+  const float* po = part_o + base * D;
+
+  // block max of the log-sum-exps
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += kCombThreads) mx = fmaxf(mx, lse[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+
+  const int d = tid % D, sg = tid / D;
+  float acc = 0.f, wpart = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kCombBatch) {
+    const int nb = min(kCombBatch, ns - s0);
+    __syncthreads();  // previous batch's weights fully read (and red[] read above)
+    for (int i = tid; i < nb; i += kCombThreads) {
+      const float w = __expf(lse[s0 + i] - mx);
+      w_lds[i] = w;
+      wpart += w;
     }
-    E::store1(o + ((size_t)b * Hq + h) * D + d, out);
+    __syncthreads();
+    const float* pb = po + (size_t)s0 * D + d;
+    int i = sg;
+    for (; i + 3 * NG < nb; i += 4 * NG) {
+      const float a0 = pb[(size_t)i * D];
+      const float a1 = pb[(size_t)(i + NG) * D];
+      const float a2 = pb[(size_t)(i + 2 * NG) * D];
+      const float a3 = pb[(size_t)(i + 3 * NG) * D];
+      acc = fmaf(w_lds[i], a0, acc);
+      acc = fmaf(w_lds[i + NG], a1, acc);
+      acc = fmaf(w_lds[i + 2 * NG], a2, acc);
+      acc = fmaf(w_lds[i + 3 * NG], a3, acc);
+    }
+    for (; i < nb; i += NG) acc = fmaf(w_lds[i], pb[(size_t)i * D], acc);
+  }
+  // block sum of the weights, group sum of the accumulators
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wpart += __shfl_xor(wpart, off, 64);
+  __syncthreads();  // every thread is past its last read of red[] and w_lds
+  if (lane == 0) red[wave] = wpart;
+  acc_lds[sg][d] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float wsum = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombThreads / 64; ++w) wsum += red[w];
+    float a = acc_lds[0][tid];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) a += acc_lds[g][tid];
+    E::store1(orow + tid, a / wsum);
   }
 }
 
@@ -666,7 +725,7 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
                      nsplit, a.c, a.neg ? 0x80008000u : 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(128), 0, stream, part_o,
+  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
                      part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, kChunkB);
   return hipGetLastError();
 }
@@ -695,7 +754,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                      a.Hq, a.Hkv, a.maxlen, nsplit, a.c, a.neg ? -1.0f : 1.0f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(128), 0, stream, part_o, part_lse,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o, part_lse,
                      a.seqlens, static_cast<T*>(a.o), a.Hq, a.maxlen, nsplit, kChunk);
   return hipGetLastError();
 }

@@ -15,22 +15,27 @@
 //     memory requirements for inference in large language models", GQA
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
-//     bf16 path (512-key chunks): the chunk streams through a ring of 32-key
-//       K/V tiles copied HBM -> LDS by global_load_lds_dwordx4 (no VGPR
-//       staging).  The ring is only two stages deep so that four workgroups
-//       (16 waves) fit per CU: on MI355X the number of resident workgroups
-//       hides the per-tile dependency chain better than a deeper ring does
-//       (chunk size, ring depth and blocks per CU are compile-time knobs).  Scores use 8 lanes per key and v_dot2_f32_bf16 (two
-//       bf16 products per instruction, no widening); values are read with the
+//     bf16 path (chunks of 1024, 512 or 256 keys, the largest that keeps
+//       two rounds of resident workgroups busy): the chunk streams through a
+//       ring of 32-key K/V tiles copied HBM -> LDS by global_load_lds_dwordx4
+//       (no VGPR staging).  The ring is only two stages deep so that four
+//       workgroups (16 waves) fit per CU: on MI355X the number of resident
+//       workgroups hides the per-tile dependency chain better than a deeper
+//       ring does.  Scores use 8 lanes per key and v_dot2_f32_bf16 (two bf16
+//       products per instruction, no widening); values are read with the
 //       transposing ds_read_b64_tr_b16 so each lane owns fixed output columns
 //       and accumulates pairs of keys with v_dot2_f32_bf16 against bf16
 //       probabilities.  Each wave keeps its own running max / sum (lazy
 //       rescale); the four waves are merged once per chunk through LDS.
+//     Each (sequence, head) row's chunk order is rotated by the row index so
+//     that the XCDs receive equal shares of real chunks.
 //     fp32 path (512-key chunks): plain VGPR loads and fp32 FMAs, 4 lanes per
 //       row for scores and 16 (or 32) lanes per row for values.
 //   kernel 2 (combine): per (sequence, query head), the partials are merged
 //     with weights exp(lse_s - max lse) -- the running-softmax rule applied to
-//     whole chunks ("11.4d FlashAttention", "Online Softmax").
+//     whole chunks ("11.4d FlashAttention", "Online Softmax"); every load in
+//     it is independent of the others, so a sequence's partials stream in at
+//     once.
 // seqlens is read only on the device; chunks at or past a sequence's length
 // exit at once, rows past the length are never loaded.
 #include "common.h"
@@ -68,7 +73,6 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<uint16_t> {  // bf16 storage
-  static constexpr int kPer16B = 8;
   __device__ static inline void widen(const u32x4& w, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -400,9 +404,6 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 
 // ---------------------------------------------------------------------------
 // bf16 split kernel: DMA ring + dot2.
-#ifndef FA_DEC_CHUNK
-#define FA_DEC_CHUNK 512
-#endif
 #ifndef FA_DEC_PASSES
 #define FA_DEC_PASSES 1
 #endif
@@ -412,7 +413,6 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 #ifndef FA_DEC_MINBLOCKS
 #define FA_DEC_MINBLOCKS 4
 #endif
-constexpr int kChunkB = FA_DEC_CHUNK;            // keys per workgroup
 constexpr int kPasses = FA_DEC_PASSES;           // 32-key passes per ring stage
 constexpr int kStageKeys = 32 * kPasses;         // keys per ring stage
 constexpr int kRingB = FA_DEC_RING;              // ring stages (kRingB - 1 in flight ahead of compute)
@@ -456,10 +456,12 @@ __device__ __forceinline__ float dpp_f(float a) {
 
 // grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
 template <int D, int GT>
-__global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
+// Eight query heads per workgroup at d = 128 need more than the 128 VGPRs of
+// four workgroups per CU; three workgroups per CU avoid spilling.
+__global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Hq, int Hkv, int maxlen, int nsplit, float c, uint32_t qflip) {
+    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip) {
   constexpr int RC = D / 8;                         // 16-byte chunks per cache row
   constexpr int STAGE = kStageKeys * D * 2;         // bytes per K (or V) stage
   constexpr int CPT = kStageKeys * RC / 256;        // DMA chunks per thread per K (or V) stage
@@ -483,9 +485,9 @@ __global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kerne
   const int b = blockIdx.z;
 
   const int L = min(max(seqlens[b], 0), maxlen);
-  const int kbeg = split * kChunkB;
+  const int kbeg = split * chunk;
   if (kbeg >= L) return;
-  const int n = min(kChunkB, L - kbeg);
+  const int n = min(chunk, L - kbeg);
   const int nst = (n + kStageKeys - 1) / kStageKeys;
   const size_t cbase = (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(kc + cbase);
@@ -709,10 +711,26 @@ __global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kerne
   }
 }
 
+// Query heads per bf16 split workgroup for a GQA group of G heads.
+int bf16_group_tile(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
+// Keys per bf16 split workgroup: the largest of 1024, 512, 256 that still
+// gives at least two full rounds of resident workgroups (4 per CU on 256
+// CUs) when every sequence is maxlen long; long chunks amortise the per-chunk
+// prologue and partials, short ones keep small batches parallel.
+int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
+  const long long rows = (long long)B * Hkv * ((Hq / Hkv) / bf16_group_tile(Hq / Hkv));
+  for (int chunk : {1024, 512}) {
+    if (rows * ((maxlen + chunk - 1) / chunk) >= 2048) return chunk;
+  }
+  return 256;
+}
+
 template <int D, int GT>
 hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
-  if (partials_bytes(a.B, a.Hq, a.maxlen, D, kChunkB) > a.ws_bytes) return hipErrorInvalidValue;
-  const int nsplit = (a.maxlen + kChunkB - 1) / kChunkB;
+  const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
+  const int nsplit = (a.maxlen + chunk - 1) / chunk;
   const int G = a.Hq / a.Hkv;
   float* part_o = static_cast<float*>(a.ws);
   const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
@@ -722,21 +740,22 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_bf16_split_kernel<D, GT>), g1, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
-                     nsplit, a.c, a.neg ? 0x80008000u : 0u);
+                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
-                     part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, kChunkB);
+                     part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, chunk);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
-  if (G % 8 == 0) return launch_bf16<D, 8>(a, stream);
-  if (G % 4 == 0) return launch_bf16<D, 4>(a, stream);
-  if (G % 2 == 0) return launch_bf16<D, 2>(a, stream);
-  return launch_bf16<D, 1>(a, stream);
+  switch (bf16_group_tile(a.Hq / a.Hkv)) {
+    case 8: return launch_bf16<D, 8>(a, stream);
+    case 4: return launch_bf16<D, 4>(a, stream);
+    case 2: return launch_bf16<D, 2>(a, stream);
+    default: return launch_bf16<D, 1>(a, stream);
+  }
 }
 
 template <typename T, int D, int GT>
@@ -769,10 +788,10 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int Hq, int maxlen, int d) {
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
   // large enough for either path's chunking
   const size_t a = partials_bytes(B, Hq, maxlen, d, kChunk);
-  const size_t b = partials_bytes(B, Hq, maxlen, d, kChunkB);
+  const size_t b = partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen));
   return a > b ? a : b;
 }
 

@@ -85,7 +85,7 @@ int decode_run(const void* q, const void* kc, const void* vc, const int32_t* seq
                int Hkv, int maxlen, int d, float scale, void* ws, size_t ws_bytes, void* stream, bool bf16) {
   int st = decode_check(q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, scale);
   if (st != FA_OK) return st;
-  const size_t need = fa::decode_workspace_bytes(B, Hq, maxlen, d);
+  const size_t need = fa::decode_workspace_bytes(B, Hq, Hkv, maxlen, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool owned = false;
   if (ws != nullptr) {
@@ -146,7 +146,7 @@ int fa_prefill_f32(const float* q, const float* k, const float* v, float* o, flo
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || maxlen <= 0 || (d != 64 && d != 128) || Hq % Hkv != 0) return 0;
-  return fa::decode_workspace_bytes(B, Hq, maxlen, d);
+  return fa::decode_workspace_bytes(B, Hq, Hkv, maxlen, d);
 }
 
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o, int B,

@@ -47,6 +47,6 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 // Keys per split-KV chunk in decode.
 constexpr int kDecodeChunk = 512;
-size_t decode_workspace_bytes(int B, int Hq, int maxlen, int d);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
 
 }  // namespace fa

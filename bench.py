@@ -70,6 +70,40 @@ def measured_traffic(name, src):
     return float(m.group(1))
 
 
+def measured_ceilings():
+    """Sustained MFMA and HBM-read rates of this device from libfa_probes.so.
+
+    The nominal peaks above assume the 2.4 GHz boost clock; under dense MFMA
+    load on random operands the part is power-limited, so the rate the matrix
+    cores actually sustain (and HBM's practical read rate) is measured here
+    and reported beside them.  Returns None if the probe library is absent.
+    """
+    import ctypes
+
+    path = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "libfa_probes.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.fa_probe_hbm_read.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.fa_probe_hbm_read.restype = ctypes.c_int
+    out = {}
+    for name, zero in (("mfma_bf16_random_operands", 0), ("mfma_bf16_zero_operands", 1)):
+        tf, ghz = ctypes.c_double(), ctypes.c_double()
+        if lib.fa_probe_mfma_bf16(zero, 20000, ctypes.byref(tf), ctypes.byref(ghz)) != 0:
+            return None
+        out[name] = {"tflops": tf.value, "shader_clock_ghz": ghz.value}
+    gbs = ctypes.c_double()
+    if lib.fa_probe_hbm_read(4 << 30, 5, ctypes.byref(gbs)) != 0:
+        return None
+    out["hbm_read_gbs"] = gbs.value
+    out["note"] = ("whole-chip sustained v_mfma_f32_32x32x16_bf16 rate (two waves per SIMD, operands in "
+                   "registers) and 4 GiB read-only stream with 16-byte loads")
+    return out
+
+
 def cpu_baseline(q, k, v, scale, seconds):
     """Time the fp64 oracle on sampled causal rows of the prefill workload."""
     import numpy as np
@@ -79,7 +113,7 @@ def cpu_baseline(q, k, v, scale, seconds):
     from exact_tiled_attention_prefill_amd.inputs import sample_rows
 
     B, Hq, N, d = q.shape
-    rows = sample_rows(N, 256, seed=3)  # ~260 rows spread over the sequence, per head
+    rows = sample_rows(N, 2048, seed=3)  # ~2100 rows spread over the sequence, per head
     heads = [(b, h) for b in range(B) for h in range(Hq)]
     done_flops, done_rows, done_heads, t0 = 0, 0, 0, time.perf_counter()
     with threadpool_limits(limits=1):
@@ -105,9 +139,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceiling"], default=None,
                     help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
-                         "copy used to calibrate the HBM byte counters")
+                         "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
+                         "MFMA / HBM ceiling probes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); nothing to do for N > 1.",
@@ -121,6 +157,9 @@ def main():
 
     load_library()  # fail loudly before any work if libfa.so is missing
     dev = torch.device("cuda:0")
+    if args.only == "ceiling":
+        print(json.dumps({"ceilings": measured_ceilings()}), flush=True)
+        return
     if args.only == "copy":
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -226,6 +265,18 @@ def main():
                                          "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC)}}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
+    if args.only is None and not args.no_ceilings:
+        ceil = measured_ceilings()
+        result["ceilings"] = ceil
+        if ceil is not None:
+            if "roofline" in result:
+                sus = ceil["mfma_bf16_random_operands"]["tflops"]
+                result["roofline"]["measured_ceiling"] = sus
+                result["roofline"]["frac_of_measured_ceiling"] = result["roofline"]["achieved"] / sus
+            if "decode" in result:
+                rl = result["decode"]["roofline"]
+                rl["measured_ceiling"] = ceil["hbm_read_gbs"]
+                rl["frac_of_measured_ceiling"] = rl["achieved"] / ceil["hbm_read_gbs"]
     if run_prefill and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)

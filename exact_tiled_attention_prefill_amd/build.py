@@ -1,7 +1,9 @@
 """Build libfa.so (the HIP kernels and the C ABI of include/fa.h) for gfx950.
 
 Each .hip source is compiled to an object with hipcc (in parallel), then
-linked into exact_tiled_attention_prefill_amd/libfa.so.  Intermediate objects
+linked into exact_tiled_attention_prefill_amd/libfa.so.  The hardware-ceiling
+probes the benchmark reports beside the nominal peaks are linked separately
+into libfa_probes.so (not part of the attention ABI).  Intermediate objects
 go to _build/ at the repository root.  Run `python -m
 exact_tiled_attention_prefill_amd.build` or call build().
 """
@@ -18,8 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+PROBE_LIB = os.path.join(PKG, "libfa_probes.so")
 
 SOURCES = ["fa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+PROBE_SOURCES = ["ceiling_probes.hip"]
 # Per-source flags.  The MFMA prefill keeps its accumulators in the VGPR form
 # of the MFMA instructions, which lets the allocator use the AGPR half of the
 # register file as overflow instead of scratch memory.
@@ -58,22 +62,27 @@ def _compile(src, extra):
     return obj, r.stderr
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every kernel source and link libfa.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    objs = [o for o, _ in results]
-    if verbose:
-        for _, err in results:
-            if err.strip():
-                print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile every kernel source, link libfa.so and libfa_probes.so; returns libfa.so's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
+    if verbose:
+        for _, err in results.values():
+            if err.strip():
+                print(err, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

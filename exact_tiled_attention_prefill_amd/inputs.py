@@ -125,3 +125,40 @@ def sample_rows(n, count, seed=0):
             break
         rows.add(int(r))
     return sorted(r for r in rows if 0 <= r < n)
+
+
+def paged_cache(kcache, vcache, seqlens, page_size, seed=0, spare_pages=2):
+    """Scatter contiguous caches [B,Hkv,maxlen,d] into a shuffled page pool.
+
+    Returns (kpages, vpages, block_table, num_pages) with pools
+    [num_pages, Hkv, page_size, d] on the caches' device and block_table
+    int32 [B, ceil(maxlen/page_size)] (CPU).  Each sequence's pages
+    0 .. ceil(L_b/page_size)-1 go to seeded random pool slots; the logical
+    rows past L_b (and past maxlen) keep whatever the contiguous cache held
+    there, NaN for caches made by decode_inputs.  `spare_pages` extra pool
+    pages are NaN, and every block-table entry past a sequence's last page
+    names one of them, so a read of anything outside the sequence is NaN.
+    Pure data movement: nothing here computes attention.
+    """
+    B, Hkv, maxlen, d = kcache.shape
+    lens = [int(x) for x in torch.as_tensor(seqlens).reshape(-1).tolist()]
+    npg = [-(-n // page_size) for n in lens]
+    max_pages = -(-maxlen // page_size)
+    used = sum(npg)
+    num_pages = used + max(1, spare_pages)
+    gen = torch.Generator().manual_seed(seed + 777)
+    slots = torch.randperm(num_pages, generator=gen).tolist()
+    kp = torch.full((num_pages, Hkv, page_size, d), float("nan"), dtype=kcache.dtype, device=kcache.device)
+    vp = torch.full_like(kp, float("nan"))
+    table = torch.full((B, max_pages), slots[used], dtype=torch.int32)
+    j = 0
+    for b in range(B):
+        for i in range(npg[b]):
+            slot = slots[j]
+            j += 1
+            r0 = i * page_size
+            rows = min(page_size, maxlen - r0)
+            kp[slot, :, :rows] = kcache[b, :, r0:r0 + rows]
+            vp[slot, :, :rows] = vcache[b, :, r0:r0 + rows]
+            table[b, i] = slot
+    return kp, vp, table, num_pages

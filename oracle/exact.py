@@ -27,7 +27,8 @@ section):
   itself is not given on the page; consecutive grouping is the reading taken.
 
 Because the fast method is exact, the reference for it is the plain
-definition (score_matrix / attention / attention_rows / decode).  The running
+definition (score_matrix / attention / attention_rows / decode /
+decode_paged).  The running
 softmax (tiled_attention) and the log-sum-exp merge (merge_partials) are
 second, independent derivations used only to pin the exactness claim and the
 split-KV merge.
@@ -172,6 +173,39 @@ def decode(q, kcache, vcache, seqlens, scale):
                 o[b, h] = (p @ vb) / l
                 lse[b, h] = m + math.log(l)
     return o, lse
+
+
+def decode_paged(q, kpages, vpages, block_table, seqlens, scale):
+    """Decode against a paged KV cache: the same attention as `decode` over
+    the logical cache the block table describes.
+
+    The retained keys and values stay available to later tokens unless the
+    runtime evicts, compresses, windows or offloads them ("How Does Flash
+    Attention Reduce Memory Traffic During Local Inference?", section
+    "Reduced IO Is Not the Same as Eliminating KV Cache"); a paged cache is
+    storage such a runtime manages.  Pool layout [num_pages, Hkv, page_size,
+    d]; block_table[b, i] is the pool page holding entries
+    i*page_size .. (i+1)*page_size - 1 of sequence b.  Only the pages that
+    hold entries 0 .. seqlens[b]-1 are read (an id past the pool raises).
+    Returns (o [B,Hq,d], lse [B,Hq]).
+    """
+    kp, vp = _f64(kpages), _f64(vpages)
+    table = np.asarray(block_table)
+    num_pages, hkv, page, d = kp.shape
+    bsz = table.shape[0]
+    lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    maxlen = max([1] + lens)
+    kc = np.zeros((bsz, hkv, maxlen, d))
+    vc = np.zeros((bsz, hkv, maxlen, d))
+    for b in range(bsz):
+        for i in range(-(-lens[b] // page)):  # pages holding entries 0 .. L-1
+            pid = int(table[b, i])
+            if not 0 <= pid < num_pages:
+                raise IndexError(f"block_table[{b}, {i}] = {pid} is outside the pool")
+            rows = min(page, lens[b] - i * page)
+            kc[b, :, i * page:i * page + rows] = kp[pid, :, :rows]
+            vc[b, :, i * page:i * page + rows] = vp[pid, :, :rows]
+    return decode(q, kc, vc, lens, scale)
 
 
 def tiled_attention(q, k, v, causal, scale, block_q, block_k):

@@ -351,3 +351,107 @@ def test_pins_catch_wrong_head_map(monkeypatch):
     ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, enable_gqa=True).numpy()
     o, _ = oracle.attention(q.numpy(), k.numpy(), v.numpy(), False, 1 / math.sqrt(3))
     assert np.abs(o - ref).max() > 1e-6
+
+
+# ---------------------------------------------------------------- P17 - P19: paged decode
+def _pool(logical_k, logical_v, lens, page, seed, spare=2):
+    """Scatter logical caches [B,Hkv,maxlen,d] into shuffled pool pages (numpy).
+
+    Unused pool pages and unused table entries are NaN pages, so reading
+    anything outside a sequence poisons the result."""
+    B, hkv, maxlen, d = logical_k.shape
+    npg = [-(-n // page) for n in lens]
+    used = sum(npg)
+    slots = np.random.default_rng(seed).permutation(used + spare)
+    kp = np.full((used + spare, hkv, page, d), np.nan)
+    vp = np.full_like(kp, np.nan)
+    table = np.full((B, -(-maxlen // page)), slots[used], dtype=np.int32)
+    j = 0
+    for b in range(B):
+        for i in range(npg[b]):
+            rows = min(page, maxlen - i * page)
+            kp[slots[j], :, :rows] = logical_k[b, :, i * page:i * page + rows]
+            vp[slots[j], :, :rows] = logical_v[b, :, i * page:i * page + rows]
+            table[b, i] = slots[j]
+            j += 1
+    return kp, vp, table
+
+
+def _paged_identical_keys_error(fn):
+    """Max error of fn against the closed form for identical keys: the mean of
+    the visible logical V rows (computed here from the logical rows)."""
+    lens, page, d, hkv, hq = [1, 4, 5, 8, 11, 0], 4, 3, 2, 4
+    B, maxlen = len(lens), 12
+    k = np.repeat(rand((1, 1, 1, d), 70), B * hkv * maxlen, axis=0).reshape(B, hkv, maxlen, d)
+    v = rand((B, hkv, maxlen, d), 71)
+    for b, n in enumerate(lens):
+        v[b, :, n:] = np.nan  # never visible
+    kp, vp, table = _pool(k, v, lens, page, seed=5)
+    q = rand((B, hq, d), 72)
+    o, _ = fn(q, kp, vp, table, lens, 0.8)
+    err = 0.0
+    for b, n in enumerate(lens):
+        for h in range(hq):
+            want = np.zeros(d) if n == 0 else v[b, h // 2, :n].mean(axis=0)
+            e = float(np.abs(o[b, h] - want).max())
+            err = max(err, e if math.isfinite(e) else math.inf)  # a NaN read counts as wrong
+    return err
+
+
+def test_paged_identical_keys_give_mean_of_logical_rows():
+    """P17: paged decode with identical keys returns the mean of the sequence's
+    logical V rows 0..L-1, across page boundaries and for L = 0."""
+    assert _paged_identical_keys_error(oracle.decode_paged) <= 1e-14
+
+
+def test_paged_needle_selects_its_logical_row():
+    """P18: one cached key scoring 50 above the rest returns its logical V row
+    (closed form (e^50 v* + sum of the others) / (e^50 + L - 1))."""
+    page, d, L = 4, 3, 13
+    for jstar in (0, 3, 4, 7, 8, 12):
+        k = np.zeros((1, 1, 16, d))
+        k[0, 0, jstar, 0] = 50.0
+        v = rand((1, 1, 16, d), 73 + jstar)
+        kp, vp, table = _pool(k, v, [L], page, seed=jstar)
+        q = np.zeros((1, 1, d))
+        q[0, 0, 0] = 1.0
+        o, lse = oracle.decode_paged(q, kp, vp, table, [L], 1.0)
+        e = math.exp(50.0)
+        want = (e * v[0, 0, jstar] + v[0, 0, :L].sum(axis=0) - v[0, 0, jstar]) / (e + L - 1)
+        assert np.abs(o[0, 0] - want).max() <= 1e-14
+        assert abs(lse[0, 0] - (50.0 + math.log(1 + (L - 1) * math.exp(-50.0)))) <= 1e-12
+
+
+def test_paged_shared_pages_and_table_tail_never_read():
+    """P19: two sequences whose tables name the same pool pages for the same
+    length give identical results; table entries past the last page are never
+    read (they hold an id outside the pool)."""
+    page, d = 8, 4
+    kp = rand((5, 1, page, d), 80)
+    vp = rand((5, 1, page, d), 81)
+    table = np.array([[3, 1, 4, 999], [3, 1, 4, -7]], dtype=np.int32)
+    q = np.repeat(rand((1, 2, d), 82), 2, axis=0)
+    o, lse = oracle.decode_paged(q, kp, vp, table, [20, 20], 0.6)
+    assert np.array_equal(o[0], o[1]) and np.array_equal(lse[0], lse[1])
+    with pytest.raises(IndexError):
+        oracle.decode_paged(q, kp, vp, table, [20, 25], 0.6)  # 25 keys need a 4th page
+
+
+def test_pins_catch_page_off_by_one():
+    """A gather that takes each sequence's pages one table entry late fails P17."""
+    def shifted(q, kp, vp, table, lens, scale):
+        t = np.asarray(table)
+        return oracle.decode_paged(q, kp, vp, np.concatenate([t[:, 1:], t[:, :1]], axis=1), lens, scale)
+    assert not _paged_identical_keys_error(shifted) <= 1e-6
+
+
+def test_paged_generator_matches_contiguous_cache():
+    """The shared paged-cache generator keeps the logical cache: the oracle
+    over its pool equals the oracle over the contiguous cache."""
+    from exact_tiled_attention_prefill_amd.inputs import paged_cache
+    q, kc, vc, lens, scale = decode_inputs(3, 4, 2, 8, 1, 40, 48, "bf16", seed=9)
+    for page in (16, 32):
+        kp, vp, table, _ = paged_cache(kc, vc, lens, page, seed=page)
+        o1, l1 = oracle.decode_paged(q, kp, vp, table, lens, scale)
+        o2, l2 = oracle.decode(q, kc, vc, lens, scale)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -2,15 +2,18 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
 One step = one fa_prefill call on the causal MHA workload (B4 H32 N4096
-d128 bf16) followed by one fa_decode call on the GQA decode workload (B64
-Hq32 Hkv8 d128 bf16, cache lengths uniform in [1024, 32768]).  Inputs are
-seeded synthetic tensors already resident in HBM before timing starts.
+d128 bf16), one fa_decode call on the GQA decode workload (B64 Hq32 Hkv8 d128
+bf16, cache lengths uniform in [1024, 32768]) and one fa_decode_paged call on
+the same logical caches in 64-key pages of a shuffled pool.  Inputs are seeded
+synthetic tensors already resident in HBM before timing starts.
 
 `value` is prefill TFLOP/s (algorithmic FLOPs = 4*d*B*Hq*(N(N+1)/2) over the
-prefill kernel's own HIP-event time); the decode figure (KV bytes read per
-second) is reported beside it.  Kernel durations come from HIP events
+prefill kernel's own HIP-event time); the decode figures (KV bytes read per
+second) are reported beside it.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  A bounded sample of the
-fp64 CPU oracle is timed on the host as a reported baseline.
+fp64 CPU oracle is timed on the host as a reported baseline, and the
+device's sustained MFMA and HBM-read rates are measured after the timed
+region.
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
@@ -140,7 +143,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "ceiling"], default=None,
+    ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "copy", "ceiling"], default=None,
                     help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
                          "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
                          "MFMA / HBM ceiling probes")
@@ -152,7 +156,8 @@ def main():
 
     import torch
 
-    from exact_tiled_attention_prefill_amd import decode, decode_workspace_bytes, load_library, prefill
+    from exact_tiled_attention_prefill_amd import (decode, decode_paged, decode_paged_workspace_bytes,
+                                                   decode_workspace_bytes, load_library, prefill)
     from exact_tiled_attention_prefill_amd import inputs as I
 
     load_library()  # fail loudly before any work if libfa.so is missing
@@ -172,6 +177,7 @@ def main():
     out = {}
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode") and not args.no_decode
+    run_paged = args.only in (None, "decode_paged") and not args.no_decode
 
     pc = I.PREFILL_MHA_4K
     if run_prefill:
@@ -184,27 +190,43 @@ def main():
             prefill(qd, kd, vd, causal=True, scale=scale, out=od, lse=lsed)
 
     dc = I.DECODE_GQA
-    if run_decode:
+    if run_decode or run_paged:
         dq, dk, dv, dl, dscale = I.decode_config_inputs(dc)
         lens_host = dl.tolist()
         dqd, dkd, dvd, dld = dq.to(dev), dk.to(dev), dv.to(dev), dl.to(dev)
         dod = torch.empty_like(dqd)
+        del dk, dv
+    if run_decode:
         ws = torch.empty(decode_workspace_bytes(dc.B, dc.Hq, dc.Hkv, dc.maxlen, dc.d), dtype=torch.uint8,
                          device=dev)
 
         def df():
             decode(dqd, dkd, dvd, dld, scale=dscale, out=dod, workspace=ws)
+    if run_paged:
+        # the same logical caches scattered over a shuffled pool of pages
+        kpd, vpd, table, _ = I.paged_cache(dkd, dvd, dl, args.page_size, seed=11)
+        tbd = table.to(dev)
+        if not run_decode:
+            del dkd, dvd
+        pws = torch.empty(decode_paged_workspace_bytes(dc.B, dc.Hq, dc.Hkv, args.page_size, table.shape[1], dc.d),
+                          dtype=torch.uint8, device=dev)
+        pod = torch.empty_like(dqd)
+
+        def pgf():
+            decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pod, workspace=pws)
 
     for _ in range(args.warmup):
         if run_prefill:
             pf()
         if run_decode:
             df()
+        if run_paged:
+            pgf()
     torch.cuda.synchronize()
 
-    # timed region: K steps, each = one prefill + one decode, events per kernel call
+    # timed region: K steps, each = one prefill + one decode (+ one paged decode), events per call
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -215,12 +237,17 @@ def main():
         if run_decode:
             df()
         ev[i][2].record(stream)
+        if run_paged:
+            pgf()
+        ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     p_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
     d_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
+    g_ms = sorted(ev[i][2].elapsed_time(ev[i][3]) for i in range(K))
     p_avg = sum(p_ms) / K
     d_avg = sum(d_ms) / K
+    g_avg = sum(g_ms) / K
 
     props = torch.cuda.get_device_properties(dev)
     result = {
@@ -237,7 +264,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) rounded to bf16)",
         "config": {"workload": pc.name, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "N": pc.N, "d": pc.d,
-                   "causal": pc.causal, "step": "one prefill (this workload) + one decode (decode.workload)"},
+                   "causal": pc.causal, "step": "one prefill (this workload) + one decode (decode.workload) + one paged decode "
+                                                              "(decode_paged.workload)"},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
@@ -265,6 +293,18 @@ def main():
                                          "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC)}}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
+    if run_paged:
+        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
+        gbs = nbytes / (g_avg * 1e-3) / 1e9
+        result["decode_paged"] = {"workload": dc.name + f"-paged{args.page_size}", "page_size": args.page_size,
+                                  "ms_avg": g_avg, "ms_median": g_ms[K // 2], "ms_min": g_ms[0],
+                                  "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                                  "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (g_avg * 1e-3),
+                                  "roofline": {"kernel": "decode_bf16_split_kernel<paged> + decode_combine_kernel",
+                                               "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+        if result["value"] is None:
+            result["value"], result["unit"] = gbs, "GB/s"
     if args.only is None and not args.no_ceilings:
         ceil = measured_ceilings()
         result["ceilings"] = ceil
@@ -273,10 +313,11 @@ def main():
                 sus = ceil["mfma_bf16_random_operands"]["tflops"]
                 result["roofline"]["measured_ceiling"] = sus
                 result["roofline"]["frac_of_measured_ceiling"] = result["roofline"]["achieved"] / sus
-            if "decode" in result:
-                rl = result["decode"]["roofline"]
-                rl["measured_ceiling"] = ceil["hbm_read_gbs"]
-                rl["frac_of_measured_ceiling"] = rl["achieved"] / ceil["hbm_read_gbs"]
+            for leg in ("decode", "decode_paged"):
+                if leg in result:
+                    rl = result[leg]["roofline"]
+                    rl["measured_ceiling"] = ceil["hbm_read_gbs"]
+                    rl["frac_of_measured_ceiling"] = rl["achieved"] / ceil["hbm_read_gbs"]
     if run_prefill and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)

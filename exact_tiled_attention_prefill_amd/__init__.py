@@ -10,6 +10,8 @@ does, and fails loudly if the library has not been built.
 from .binding import (  # noqa: F401
     FaError,
     decode,
+    decode_paged,
+    decode_paged_workspace_bytes,
     decode_workspace_bytes,
     library_path,
     load_library,

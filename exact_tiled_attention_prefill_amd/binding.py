@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_decode_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_decode_f32_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
 }
 
 _lib = None
@@ -195,4 +197,48 @@ def decode(q, kcache, vcache, seqlens, scale=None, out=None, workspace=None, str
         fn = lib.fa_decode_ws if bf16 else lib.fa_decode_f32_ws
         st = fn(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream))
     _check(st, fn.__name__)
+    return out
+
+
+def decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d):
+    return int(load_library().fa_decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d))
+
+
+def decode_paged(q, kpages, vpages, block_table, seqlens, scale=None, out=None, workspace=None, stream=None):
+    """One query token per sequence against a paged KV cache (bf16).
+
+    q [B,Hq,d]; kpages/vpages [num_pages,Hkv,page_size,d]; block_table int32
+    [B,max_pages] and seqlens int32 [B], both on the device.  `workspace`
+    (uint8 device tensor of at least decode_paged_workspace_bytes(...)
+    bytes) avoids the library's stream-ordered allocation.  Returns o [B,Hq,d].
+    """
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(kpages, "kpages", torch.bfloat16, 4)
+    _require(vpages, "vpages", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, d = q.shape
+    num_pages, Hkv, page_size, _ = kpages.shape
+    if tuple(kpages.shape) != (num_pages, Hkv, page_size, d) or tuple(vpages.shape) != tuple(kpages.shape):
+        raise ValueError("kpages/vpages must be [num_pages, Hkv, page_size, d] matching q")
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages] and seqlens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3)
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+            raise TypeError("workspace must be a uint8 device tensor")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    lib = load_library()
+    st = lib.fa_decode_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(block_table), _ptr(seqlens), _ptr(out),
+                             B, Hq, Hkv, num_pages, page_size, max_pages, d, float(scale), ws_ptr, ws_bytes,
+                             _stream_ptr(stream))
+    _check(st, "fa_decode_paged")
     return out

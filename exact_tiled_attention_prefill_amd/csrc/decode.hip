@@ -433,6 +433,15 @@ __device__ __forceinline__ void dec_dma16(const void* base, uint32_t off, uint8_
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
   asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
+// the same copy from a per-lane 64-bit address (paged caches: the rows of one
+// stage may come from different pages)
+__device__ __forceinline__ void dec_dma16_addr(const void* addr, uint8_t* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
+}
+// Most pool pages one chunk touches: 1024 keys over pages of >= 16 keys, plus
+// one page for a chunk that does not start on a page boundary.
+constexpr int kMaxChunkPages = 1024 / 16 + 1;
 typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
   typedef __attribute__((address_space(3))) dec_i16x4 lds_t;
@@ -455,13 +464,14 @@ __device__ __forceinline__ float dpp_f(float a) {
 }
 
 // grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
-template <int D, int GT>
+// PAGED: kc / vc are page pools and pg maps logical pages to pool pages.
+template <int D, int GT, bool PAGED>
 // Eight query heads per workgroup at d = 128 need more than the 128 VGPRs of
 // four workgroups per CU; three workgroups per CU avoid spilling.
 __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip) {
+    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg) {
   constexpr int RC = D / 8;                         // 16-byte chunks per cache row
   constexpr int STAGE = kStageKeys * D * 2;         // bytes per K (or V) stage
   constexpr int CPT = kStageKeys * RC / 256;        // DMA chunks per thread per K (or V) stage
@@ -472,6 +482,7 @@ __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingB][2][STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][GT][8];
   __shared__ float m_w[4][GT], l_w[4][GT];
+  __shared__ int pid_lds[PAGED ? kMaxChunkPages : 1];
   static_assert(4 * GT * D * 4 <= kRingB * 2 * STAGE, "wave partials must fit in the ring");
 
   const int tid = threadIdx.x;
@@ -489,9 +500,18 @@ __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) 
   if (kbeg >= L) return;
   const int n = min(chunk, L - kbeg);
   const int nst = (n + kStageKeys - 1) / kStageKeys;
-  const size_t cbase = (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
+  const size_t cbase = PAGED ? 0 : (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
   const uint8_t* kp = reinterpret_cast<const uint8_t*>(kc + cbase);
   const uint8_t* vp = reinterpret_cast<const uint8_t*>(vc + cbase);
+  // paged: this chunk's slice of the block table, pool ids clamped into the
+  // pool so that a bad table can never address outside it
+  const int slot0 = PAGED ? (kbeg >> pg.page_shift) : 0;
+  if (PAGED) {
+    const int nslots = ((kbeg + n - 1) >> pg.page_shift) - slot0 + 1;  // <= kMaxChunkPages
+    if (tid < nslots)
+      pid_lds[tid] = min(max(pg.block_table[(size_t)b * pg.max_pages + slot0 + tid], 0), pg.num_pages - 1);
+    __syncthreads();
+  }
 
   // ---- score layout: key kk = lane/8 of the wave's 8 keys, part j = lane%8 (EPL elements) ----
   const int kk = lane >> 3;
@@ -548,7 +568,19 @@ __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) 
     const uint8_t* vb = vp + (size_t)r0 * D * 2;
     uint8_t* kl = ring[st % kRingB][0];
     uint8_t* vl = ring[st % kRingB][1];
-    if (r0 + kStageKeys <= n) {
+    if (PAGED) {
+      // row r of the stage is cache entry kbeg + r0 + r (the last valid entry
+      // for rows past the end): pool page, then the row within the page
+      const int pmask = (1 << pg.page_shift) - 1;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int key = kbeg + r0 + min(drow[i], n - 1 - r0);
+        const int pid = pid_lds[(key >> pg.page_shift) - slot0];
+        const size_t row = ((((size_t)pid * Hkv + kvh) << pg.page_shift) | (size_t)(key & pmask)) * (D * 2);
+        dec_dma16_addr(kp + row + (dk[i] - drow[i] * D * 2), kl + (i * 256 + wave_s * 64) * 16);
+        dec_dma16_addr(vp + row + (dv[i] - drow[i] * D * 2), vl + (i * 256 + wave_s * 64) * 16);
+      }
+    } else if (r0 + kStageKeys <= n) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         dec_dma16(kb, dk[i], kl + (i * 256 + wave_s * 64) * 16);
@@ -726,7 +758,7 @@ int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   return 256;
 }
 
-template <int D, int GT>
+template <int D, int GT, bool PAGED>
 hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
   if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
@@ -737,10 +769,10 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
   dim3 g1(nsplit, a.Hkv * (G / GT), a.B);
   if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_bf16_split_kernel<D, GT>), g1, dim3(256), 0, stream,
+  hipLaunchKernelGGL((decode_bf16_split_kernel<D, GT, PAGED>), g1, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
-                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u);
+                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u, a.paged);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
@@ -748,13 +780,13 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
   switch (bf16_group_tile(a.Hq / a.Hkv)) {
-    case 8: return launch_bf16<D, 8>(a, stream);
-    case 4: return launch_bf16<D, 4>(a, stream);
-    case 2: return launch_bf16<D, 2>(a, stream);
-    default: return launch_bf16<D, 1>(a, stream);
+    case 8: return launch_bf16<D, 8, PAGED>(a, stream);
+    case 4: return launch_bf16<D, 4, PAGED>(a, stream);
+    case 2: return launch_bf16<D, 2, PAGED>(a, stream);
+    default: return launch_bf16<D, 1, PAGED>(a, stream);
   }
 }
 
@@ -796,8 +828,16 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_bf16_g<128>(a, stream);
-  if (a.d == 64) return launch_bf16_g<64>(a, stream);
+  if (a.paged.block_table != nullptr) {
+    if (a.paged.page_shift < 4 || a.paged.num_pages <= 0 || a.paged.max_pages <= 0 ||
+        a.maxlen != (a.paged.max_pages << a.paged.page_shift))
+      return hipErrorInvalidValue;
+    if (a.d == 128) return launch_bf16_g<128, true>(a, stream);
+    if (a.d == 64) return launch_bf16_g<64, true>(a, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a.d == 128) return launch_bf16_g<128, false>(a, stream);
+  if (a.d == 64) return launch_bf16_g<64, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -82,7 +82,8 @@ int decode_check(const void* q, const void* kc, const void* vc, const int32_t* s
 }
 
 int decode_run(const void* q, const void* kc, const void* vc, const int32_t* seqlens, void* o, int B, int Hq,
-               int Hkv, int maxlen, int d, float scale, void* ws, size_t ws_bytes, void* stream, bool bf16) {
+               int Hkv, int maxlen, int d, float scale, void* ws, size_t ws_bytes, void* stream, bool bf16,
+               fa::PagedKV paged = fa::PagedKV{}) {
   int st = decode_check(q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, scale);
   if (st != FA_OK) return st;
   const size_t need = fa::decode_workspace_bytes(B, Hq, Hkv, maxlen, d);
@@ -102,13 +103,24 @@ int decode_run(const void* q, const void* kc, const void* vc, const int32_t* seq
     owned = true;
   }
   fa::DecodeArgs a{q, kc, vc, seqlens, o, B, Hq, Hkv, maxlen, d, softmax_coeff(scale), scale < 0.f, ws,
-                   owned ? need : ws_bytes};
+                   owned ? need : ws_bytes, paged};
   hipError_t e = bf16 ? fa::launch_decode_bf16(a, s) : fa::launch_decode_f32(a, s);
   if (owned) {
     hipError_t f = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = f;
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// Paged-cache geometry: page_size a power of two in [16, 2^20], logical
+// length max_pages * page_size within int.  Returns the page shift, or -1.
+int paged_shift(int num_pages, int page_size, int max_pages) {
+  if (num_pages <= 0 || max_pages <= 0 || page_size < 16 || page_size > (1 << 20)) return -1;
+  if ((page_size & (page_size - 1)) != 0) return -1;
+  if ((long long)max_pages * page_size > 0x7fffffffLL) return -1;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  return shift;
 }
 
 }  // namespace
@@ -160,6 +172,25 @@ int fa_decode_ws(const void* q, const void* kcache, const void* vcache, const in
   if (workspace == nullptr) return FA_ERR_INVALID_ARG;
   return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, workspace, workspace_bytes,
                     stream, true);
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int page_size, int max_pages, int d) {
+  if (paged_shift(1, page_size, max_pages) < 0) return 0;
+  return fa_decode_workspace_bytes(B, Hq, Hkv, max_pages * page_size, d);
+}
+
+int fa_decode_paged(const void* q, const void* kpages, const void* vpages, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int num_pages, int page_size,
+                    int max_pages, int d, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int shift = paged_shift(num_pages, page_size, max_pages);
+  if (shift < 0 || block_table == nullptr || !aligned(block_table, 4)) return FA_ERR_INVALID_ARG;
+  fa::PagedKV pg;
+  pg.block_table = block_table;
+  pg.max_pages = max_pages;
+  pg.num_pages = num_pages;
+  pg.page_shift = shift;
+  return decode_run(q, kpages, vpages, seqlens, o, B, Hq, Hkv, max_pages * page_size, d, scale, workspace,
+                    workspace_bytes, stream, true, pg);
 }
 
 int fa_decode_f32(const float* q, const float* kcache, const float* vcache, const int32_t* seqlens, float* o,

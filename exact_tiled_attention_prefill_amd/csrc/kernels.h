@@ -27,17 +27,29 @@ struct PrefillArgs {
   bool neg;      // scale < 0: use -q
 };
 
+// Paged KV cache: k/v point at page pools [num_pages, Hkv, page_size, d];
+// block_table [B, max_pages] maps a sequence's logical page i (cache entries
+// i*page_size .. (i+1)*page_size - 1) to a pool page.  block_table == nullptr
+// means the contiguous layout [B, Hkv, maxlen, d].
+struct PagedKV {
+  const int32_t* block_table = nullptr;
+  int max_pages = 0;
+  int num_pages = 0;
+  int page_shift = 0;  // page_size = 1 << page_shift
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
   const int32_t* seqlens;
   void* o;
-  int B, Hq, Hkv, maxlen, d;
+  int B, Hq, Hkv, maxlen, d;  // paged: maxlen = max_pages * page_size
   float c;
   bool neg;
   void* ws;        // >= decode_workspace_bytes(...)
   size_t ws_bytes; // size of ws; each launch checks its own partial layout fits
+  PagedKV paged;   // bf16 only
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

@@ -126,6 +126,44 @@ int fa_decode_f32_ws(const float* q, const float* kcache, const float* vcache,
  * (0 if the sizes are invalid). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
 
+/*
+ * Decode against a paged KV cache.  The retained history stays available to
+ * later tokens unless the runtime evicts, compresses, windows or offloads it
+ * ("How Does Flash Attention Reduce Memory Traffic During Local Inference?",
+ * section "Reduced IO Is Not the Same as Eliminating KV Cache"); a paged
+ * cache is the storage such a runtime manages: fixed-size pages from one
+ * pool, mapped to each sequence by a block table, so pages can be freed,
+ * moved or shared without copying a sequence's whole history.  The attention
+ * computed is exactly fa_decode's over the logical cache the table describes.
+ *   q           [B, Hq, d]                        bf16
+ *   kpages      [num_pages, Hkv, page_size, d]    bf16 page pool (page p holds
+ *   vpages      [num_pages, Hkv, page_size, d]    bf16  page_size consecutive
+ *                                                 cache entries of every KV head)
+ *   block_table [B, max_pages]                    int32, device memory: entry
+ *               i of row b is the pool page holding cache entries
+ *               i*page_size .. (i+1)*page_size - 1 of sequence b.  Entries
+ *               past the sequence's last page are never read; several rows
+ *               may name the same page (shared prefixes).  Ids outside
+ *               [0, num_pages) are a caller error and are clamped into the
+ *               pool on the device (never an out-of-bounds read).
+ *   seqlens     [B]                               int32, device memory, clamped
+ *               to [0, max_pages * page_size]; 0 gives o = 0.
+ *   o           [B, Hq, d]                        bf16 (written)
+ * page_size must be a power of two in [16, 2^20]; max_pages * page_size must
+ * fit in an int.  workspace may be NULL (then it is obtained stream-ordered,
+ * as in fa_decode) or hold at least fa_decode_paged_workspace_bytes(...)
+ * bytes, 256-byte aligned.  Work: two kernel launches on `stream`.
+ */
+int fa_decode_paged(const void* q, const void* kpages, const void* vpages,
+                    const int32_t* block_table, const int32_t* seqlens, void* o,
+                    int B, int Hq, int Hkv, int num_pages, int page_size,
+                    int max_pages, int d, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_decode_paged needs (0 if the sizes are invalid). */
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int page_size,
+                                       int max_pages, int d);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int fa_version(void);
 

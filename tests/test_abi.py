@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fa_prefill", "fa_decode", "fa_prefill_f32", "fa_decode_f32", "fa_decode_ws",
-              "fa_decode_f32_ws", "fa_decode_workspace_bytes", "fa_strerror", "fa_version"):
+              "fa_decode_f32_ws", "fa_decode_workspace_bytes", "fa_decode_paged",
+              "fa_decode_paged_workspace_bytes", "fa_strerror", "fa_version"):
         assert n in names
     assert set(names) == set(binding.SIGNATURES)
 
@@ -147,6 +148,50 @@ def test_workspace_bytes():
     assert lib.fa_decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
     assert lib.fa_decode_workspace_bytes(64, 32, 5, 32768, 128) == 0
     assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 96) == 0
+
+
+def paged_call(fn, **kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, sl=P, o=P, B=2, Hq=8, Hkv=2, num_pages=64, page=32, max_pages=32, d=128,
+             scale=0.1, w=None, wb=0)
+    a.update(kw)
+    return fn(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["o"], a["B"], a["Hq"], a["Hkv"], a["num_pages"],
+              a["page"], a["max_pages"], a["d"], ctypes.c_float(a["scale"]), a["w"], a["wb"], None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(kp=None), binding.FA_ERR_INVALID_ARG),
+    (dict(vp=None), binding.FA_ERR_INVALID_ARG),
+    (dict(bt=None), binding.FA_ERR_INVALID_ARG),
+    (dict(bt=ctypes.c_void_p(0x10002)), binding.FA_ERR_INVALID_ARG),
+    (dict(sl=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(page=24), binding.FA_ERR_INVALID_ARG),
+    (dict(page=8), binding.FA_ERR_INVALID_ARG),
+    (dict(page=0), binding.FA_ERR_INVALID_ARG),
+    (dict(page=1 << 21), binding.FA_ERR_INVALID_ARG),
+    (dict(num_pages=0), binding.FA_ERR_INVALID_ARG),
+    (dict(max_pages=0), binding.FA_ERR_INVALID_ARG),
+    (dict(max_pages=1 << 27, page=64), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=8, Hkv=3), binding.FA_ERR_INVALID_ARG),
+    (dict(kp=P_MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(w=P, wb=16), binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), binding.FA_ERR_UNSUPPORTED),
+])
+def test_decode_paged_rejects_invalid_arguments(kw, code):
+    assert paged_call(binding.load_library().fa_decode_paged, **kw) == code
+
+
+@needs_lib
+def test_paged_workspace_bytes():
+    lib = binding.load_library()
+    for page, pages in ((16, 2048), (64, 512), (1024, 32)):
+        assert lib.fa_decode_paged_workspace_bytes(64, 32, 8, page, pages, 128) == \
+            lib.fa_decode_workspace_bytes(64, 32, 8, page * pages, 128)
+    assert lib.fa_decode_paged_workspace_bytes(64, 32, 8, 24, 100, 128) == 0
+    assert lib.fa_decode_paged_workspace_bytes(64, 32, 8, 64, 0, 128) == 0
+    assert lib.fa_decode_paged_workspace_bytes(64, 32, 5, 64, 10, 128) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -162,3 +162,22 @@ def paged_cache(kcache, vcache, seqlens, page_size, seed=0, spare_pages=2):
             vp[slot, :, :rows] = vcache[b, :, r0:r0 + rows]
             table[b, i] = slot
     return kp, vp, table, num_pages
+
+
+def varlen_inputs(lens, Hq, Hkv, d, dtype="bf16", seed=0):
+    """Packed variable-length inputs for sequences lens = [(n_q, n_k), ...].
+
+    Returns (q [total_q,Hq,d], k, v [total_k,Hkv,d], cu_q, cu_k int32 [B+1],
+    scale) as CPU tensors; Q, K, V are each one seeded N(0,1) draw of the
+    packed shape, rounded to bf16 (or fp32).  The queries of a sequence are
+    its last n_q positions (n_q < n_k: a chunk against a cached prefix).
+    """
+    gen = torch.Generator().manual_seed(seed)
+    tq = sum(nq for nq, _ in lens)
+    tk = sum(nk for _, nk in lens)
+    q = _draw(gen, (tq, Hq, d), dtype)
+    k = _draw(gen, (tk, Hkv, d), dtype)
+    v = _draw(gen, (tk, Hkv, d), dtype)
+    cu_q = torch.tensor([0] + [sum(nq for nq, _ in lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32)
+    cu_k = torch.tensor([0] + [sum(nk for _, nk in lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32)
+    return q, k, v, cu_q, cu_k, fp32_scale(d)

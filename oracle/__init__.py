@@ -8,8 +8,9 @@ leg of the benchmark use it.  It shares no code with the GPU path.
 Modules
 -------
 exact       the definition written out: materialised score matrix, softmax,
-            weighted sum of values (prefill and KV-cache decode, contiguous
-            or paged), plus the
+            weighted sum of values (prefill, packed variable-length prefill
+            with bottom-right causal alignment and a left window, KV-cache
+            decode contiguous or paged), plus the
             tile-by-tile running-softmax form and the log-sum-exp merge of
             partial results that the exactness claim rests on.
 traffic     the page-1 tiled-GEMM load-count model.
@@ -22,6 +23,8 @@ scaled_dot_product_attention.
 from .exact import (  # noqa: F401
     attention,
     attention_rows,
+    attention_varlen,
+    varlen_visible,
     decode,
     decode_paged,
     score_matrix,

@@ -28,7 +28,7 @@ section):
 
 Because the fast method is exact, the reference for it is the plain
 definition (score_matrix / attention / attention_rows / decode /
-decode_paged).  The running
+decode_paged / attention_varlen).  The running
 softmax (tiled_attention) and the log-sum-exp merge (merge_partials) are
 second, independent derivations used only to pin the exactness claim and the
 split-KV merge.
@@ -139,6 +139,62 @@ def attention_rows(q, k, v, causal, scale, rows, heads=None):
             l = p.sum()
             o[t, r] = (p @ vb[:nk]) / l
             lse[t, r] = m + math.log(l)
+    return o, lse
+
+
+def varlen_visible(i, n_q, n_k, causal, window_left):
+    """Keys query row i of a sequence (n_q queries, n_k keys) may see: [lo, hi].
+
+    The queries are the last n_q positions of the sequence, so with
+    off = n_k - n_q, causal row i sees keys up to i + off (bottom-right
+    alignment: a chunk of new queries sees the cached prefix and itself).
+    A left window W >= 0 also drops keys before i + off - W.  The range may
+    be empty (hi < lo), e.g. causal rows with i + off < 0.
+    """
+    off = n_k - n_q
+    hi = min(i + off, n_k - 1) if causal else n_k - 1
+    lo = max(0, i + off - window_left) if window_left >= 0 else 0
+    return lo, hi
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1):
+    """Packed variable-length attention (chunked prefill, sliding window).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d]; sequence b owns query rows
+    cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1.  Row i of a
+    sequence attends to the keys varlen_visible gives, with the scale,
+    mask and softmax of `attention`.  The retained cache a chunk of new
+    queries attends to, and windowing as one of the ways a runtime may limit
+    it, follow "How Does Flash Attention Reduce Memory Traffic During Local
+    Inference?", section "Reduced IO Is Not the Same as Eliminating KV
+    Cache"; the masked softmax, its section "Kernel Fusion Keeps More of the
+    Attention Chain in One Execution Path".  A row that sees no key gets
+    o = 0 and lse = -inf.  Returns (o [total_q, Hq, d], lse [Hq, total_q]).
+    """
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    total_q, hq, d = qf.shape
+    hkv = kf.shape[1]
+    cu_q = [int(x) for x in np.asarray(cu_q).reshape(-1)]
+    cu_k = [int(x) for x in np.asarray(cu_k).reshape(-1)]
+    o = np.zeros((total_q, hq, d))
+    lse = np.full((hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, n_q = cu_q[b], cu_q[b + 1] - cu_q[b]
+        k0, n_k = cu_k[b], cu_k[b + 1] - cu_k[b]
+        for h in range(hq):
+            g = _kv_head(h, hq, hkv)
+            kb = kf[k0:k0 + n_k, g]
+            vb = vf[k0:k0 + n_k, g]
+            for i in range(n_q):
+                lo, hi = varlen_visible(i, n_q, n_k, causal, window_left)
+                if hi < lo:
+                    continue
+                s = float(scale) * (kb[lo:hi + 1] @ qf[q0 + i, h])
+                m = s.max()
+                p = np.exp(s - m)
+                l = p.sum()
+                o[q0 + i, h] = (p @ vb[lo:hi + 1]) / l
+                lse[h, q0 + i] = m + math.log(l)
     return o, lse
 
 

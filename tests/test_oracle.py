@@ -455,3 +455,92 @@ def test_paged_generator_matches_contiguous_cache():
         o1, l1 = oracle.decode_paged(q, kp, vp, table, lens, scale)
         o2, l2 = oracle.decode(q, kc, vc, lens, scale)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------- P20 - P24: packed variable-length prefill
+def _pack(seqs_q, seqs_k):
+    """Per-sequence arrays [n, H, d] -> packed arrays and cumulative offsets."""
+    cu_q = np.cumsum([0] + [len(x) for x in seqs_q])
+    cu_k = np.cumsum([0] + [len(x) for x in seqs_k])
+    return np.concatenate(seqs_q), np.concatenate(seqs_k), cu_q, cu_k
+
+
+@pytest.mark.parametrize("lens", [[(5, 9), (7, 7), (1, 12)], [(16, 40), (33, 33)]])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1)])
+def test_varlen_causal_matches_torch_lower_right(lens, hq, hkv):
+    """P20: causal varlen rows equal PyTorch CPU float64 SDPA with its own
+    bottom-right causal bias (torch.nn.attention.bias.causal_lower_right),
+    sequence by sequence, GQA by repeating K/V heads."""
+    from torch.nn.attention.bias import causal_lower_right
+    d, scale = 8, 0.41
+    qs = [rand((nq, hq, d), 100 + i) for i, (nq, _) in enumerate(lens)]
+    ks = [rand((nk, hkv, d), 200 + i) for i, (_, nk) in enumerate(lens)]
+    vs = [rand((nk, hkv, d), 300 + i) for i, (_, nk) in enumerate(lens)]
+    q, k, cu_q, cu_k = _pack(qs, ks)
+    v = np.concatenate(vs)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, True, scale)
+    for b, (nq, nk) in enumerate(lens):
+        tq = torch.from_numpy(qs[b]).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(np.repeat(ks[b], hq // hkv, axis=1)).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(np.repeat(vs[b], hq // hkv, axis=1)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=causal_lower_right(nq, nk), scale=scale)[0].permute(1, 0, 2).numpy()
+        assert np.abs(o[cu_q[b]:cu_q[b + 1]] - ref).max() <= 1e-12
+
+
+def test_varlen_window_zero_returns_diagonal_value():
+    """P21: window 0 under the causal mask leaves one key per row, key i + off:
+    o = V[i + off], lse = scale * q_i . k_{i + off} (closed form)."""
+    d, nq, nk, scale = 5, 6, 10, 0.7
+    q, k, v = rand((nq, 2, d), 400), rand((nk, 1, d), 401), rand((nk, 1, d), 402)
+    o, lse = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], True, scale, window_left=0)
+    for i in range(nq):
+        j = i + nk - nq
+        for h in range(2):
+            assert np.array_equal(o[i, h], v[j, 0])
+            assert abs(lse[h, i] - scale * q[i, h] @ k[j, 0]) <= 1e-14
+
+
+@pytest.mark.parametrize("w", [1, 3, 50])
+def test_varlen_window_identical_keys_give_window_mean(w):
+    """P22: identical keys -> uniform weights over the window
+    [max(0, i+off-W), i+off]: o = mean of those V rows, lse = s + ln(count)."""
+    d, nq, nk, scale = 4, 7, 12, 0.3
+    q = rand((nq, 1, d), 410)
+    k = np.repeat(rand((1, 1, d), 411), nk, axis=0)
+    v = rand((nk, 1, d), 412)
+    o, lse = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], True, scale, window_left=w)
+    for i in range(nq):
+        hi = i + nk - nq
+        lo = max(0, hi - w)
+        assert np.abs(o[i, 0] - v[lo:hi + 1, 0].mean(axis=0)).max() <= 1e-14
+        assert abs(lse[0, i] - (scale * q[i, 0] @ k[0, 0] + math.log(hi - lo + 1))) <= 1e-13
+
+
+def test_varlen_rows_without_keys_and_chunking():
+    """P23: causal rows with i + (n_k - n_q) < 0 see no key (o = 0, lse = -inf);
+    the last n_q rows of a full causal prefill equal a chunk of n_q queries
+    against the whole key prefix (dense oracle, itself pinned against SDPA)."""
+    d, n, scale = 6, 20, 0.5
+    q, k, v = rand((1, 2, n, d), 420), rand((1, 1, n, d), 421), rand((1, 1, n, d), 422)
+    full_o, full_l = oracle.attention(q, k, v, True, scale)
+    qp, kp, vp = (x[0].transpose(1, 0, 2) for x in (q, k, v))  # [n, H, d]
+    for nq in (1, 7, 20):
+        o, lse = oracle.attention_varlen(qp[n - nq:], kp, vp, [0, nq], [0, n], True, scale)
+        assert np.abs(o - full_o[0][:, n - nq:].transpose(1, 0, 2)).max() <= 1e-13
+        assert np.abs(lse - full_l[0][:, n - nq:]).max() <= 1e-13
+    # more queries than keys: the first 3 rows see nothing
+    o, lse = oracle.attention_varlen(qp[:8], kp[:5], vp[:5], [0, 8], [0, 5], True, scale)
+    assert np.all(o[:3] == 0) and np.all(np.isneginf(lse[:, :3]))
+    assert np.isfinite(lse[:, 3:]).all()
+
+
+def test_pins_catch_window_off_by_one(monkeypatch):
+    """A window that keeps one key too many fails P21."""
+    real = oatt.varlen_visible
+    monkeypatch.setattr(oatt, "varlen_visible",
+                        lambda i, nq, nk, c, w: real(i, nq, nk, c, w + 1 if w >= 0 else w))
+    d, nq, nk = 5, 6, 10
+    q, k, v = rand((nq, 1, d), 400), rand((nk, 1, d), 401), rand((nk, 1, d), 402)
+    o, _ = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], True, 0.7, window_left=0)
+    assert not np.array_equal(o[1, 0], v[1 + nk - nq, 0])

@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     prefill,
+    prefill_varlen,
 )

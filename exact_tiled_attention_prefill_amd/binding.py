@@ -31,6 +31,8 @@ SIGNATURES = {
     "fa_decode_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_decode_f32_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_prefill_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                               _vp]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
 }
@@ -242,3 +244,44 @@ def decode_paged(q, kpages, vpages, block_table, seqlens, scale=None, out=None, 
                              _stream_ptr(stream))
     _check(st, "fa_decode_paged")
     return out
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, window_left=-1,
+                   scale=None, out=None, lse=None, return_lse=True, stream=None):
+    """Packed variable-length attention (bf16): chunked prefill, sliding window.
+
+    q [total_q,Hq,d]; k/v [total_k,Hkv,d]; cu_seqlens_q/k int32 [B+1] on the
+    device; a sequence's queries are its last n_q positions (causal row i
+    sees keys <= i + n_k - n_q, and >= that minus window_left when
+    window_left >= 0).  Returns o [total_q,Hq,d] and, if return_lse, lse
+    [Hq,total_q] (fp32).
+    """
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k, "k", torch.bfloat16, 3)
+    _require(v, "v", torch.bfloat16, 3)
+    _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    if tuple(k.shape) != (total_k, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v must be [total_k, Hkv, d] matching q")
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 1 or cu_seqlens_k.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2)
+    st = load_library().fa_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if lse is not None else None, _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, int(bool(causal)),
+        int(window_left), float(scale), _stream_ptr(stream))
+    _check(st, "fa_prefill_varlen")
+    return (out, lse) if return_lse else out

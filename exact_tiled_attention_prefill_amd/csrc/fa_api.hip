@@ -156,6 +156,36 @@ int fa_prefill_f32(const float* q, const float* k, const float* v, float* o, flo
   return prefill_common(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream, false);
 }
 
+int fa_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq, int Hkv,
+                      int total_q, int total_k, int max_seqlen_q, int d, int causal, int window_left,
+                      float scale, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_q > total_q || window_left < -1)
+    return FA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, d, scale);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(cu_seqlens_k, 4))
+    return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  // one 64-key tile of packed K rows must be addressable with 32-bit offsets
+  if ((long long)64 * Hkv * d * 2 > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Hq * ((max_seqlen_q + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, d, causal != 0, softmax_coeff(scale), scale < 0.f};
+  a.varlen.cu_q = cu_seqlens_q;
+  a.varlen.cu_k = cu_seqlens_k;
+  a.varlen.total_q = total_q;
+  a.varlen.total_k = total_k;
+  a.varlen.window = window_left;
+  return fa::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || maxlen <= 0 || (d != 64 && d != 128) || Hq % Hkv != 0) return 0;
   return fa::decode_workspace_bytes(B, Hq, Hkv, maxlen, d);

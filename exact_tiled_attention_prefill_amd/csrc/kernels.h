@@ -15,16 +15,30 @@ namespace fa {
 // exponent of a finite score to 0 exactly as a zero scale would.
 constexpr float kMinC = 1e-30f;
 
+// Packed variable-length sequences: q/o [total_q, Hq, d], k/v [total_k, Hkv, d],
+// lse [Hq, total_q]; sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key
+// rows cu_k[b] .. cu_k[b+1]-1 (device arrays; clamped into range on the
+// device).  Its queries are the last n_q positions (causal row i sees keys up
+// to i + n_k - n_q); window >= 0 also drops keys before that bound - window.
+struct VarlenRef {
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0;
+  int total_k = 0;
+  int window = -1;
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;  // may be null
-  int B, Hq, Hkv, N, d;
+  int B, Hq, Hkv, N, d;  // varlen: N = the longest sequence's query count
   bool causal;
   float c;       // |scale| * log2(e), >= kMinC
   bool neg;      // scale < 0: use -q
+  VarlenRef varlen;  // cu_q == nullptr: dense [B, H, N, d] layout (bf16 only otherwise)
 };
 
 // Paged KV cache: k/v point at page pools [num_pages, Hkv, page_size, d];

@@ -123,11 +123,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* l
   asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
 
-template <int D, bool CAUSAL>
+// VARLEN: packed variable-length sequences (VarlenRef); N is then the longest
+// sequence's query count, which sizes the grid.
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int Hq, int Hkv, int N, int n_qtiles, int n_items, float c, uint32_t qflip) {
+    int Hq, int Hkv, int N, int n_qtiles, int n_items, float c, uint32_t qflip, VarlenRef vr) {
   constexpr int KS = D / 16;                // k-steps of S^T = K Q^T
   constexpr int MD = D / 32;                // 32-row blocks of O^T
   constexpr int RC = D / 8;                 // 16-byte chunks per row
@@ -158,30 +160,48 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const int g = grp - b * Hkv;
   const int h = g * G + (rem - tslot * G);
   const int bh = b * Hq + h;
-  const size_t qbase = (size_t)bh * N * D;
+
+  // ---- sequence geometry: Lq queries (the last Lq positions) against Lk keys;
+  // causal row i sees keys up to i + off, a window W >= 0 none before i + off - W.
+  // Dense: Lq = Lk = N, off = 0, no window; packed rows have stride H*D. ----
+  int Lq = N, Lk = N, qstart = 0, kstart = 0;
+  if (VARLEN) {
+    qstart = min(max(vr.cu_q[b], 0), vr.total_q);
+    const int qe = min(max(vr.cu_q[b + 1], qstart), vr.total_q);
+    kstart = min(max(vr.cu_k[b], 0), vr.total_k);
+    const int ke = min(max(vr.cu_k[b + 1], kstart), vr.total_k);
+    Lq = qe - qstart;
+    Lk = ke - kstart;
+  }
+  const int off = Lk - Lq;
+  const int W = VARLEN ? vr.window : -1;
+  const int q_rs = VARLEN ? Hq * D : D;   // row strides (elements)
+  const int kv_rs = VARLEN ? Hkv * D : D;
+  const size_t qbase = VARLEN ? ((size_t)qstart * Hq + h) * D : (size_t)bh * N * D;
   const uint16_t* qh = q + qbase;
-  const uint16_t* kh = k + (size_t)grp * N * D;
-  const uint16_t* vh = v + (size_t)grp * N * D;
+  const uint16_t* kh = k + (VARLEN ? ((size_t)kstart * Hkv + g) * D : (size_t)grp * N * D);
+  const uint16_t* vh = v + (VARLEN ? ((size_t)kstart * Hkv + g) * D : (size_t)grp * N * D);
 
   // Rows of this wave: q0 + wave + kWaves*j; lane column x holds row q0 + wave + kWaves*x.
   const int q0 = qtile * kBR;
+  if (VARLEN && q0 >= Lq) return;  // a shorter sequence: the whole workgroup leaves
   const int qrow = q0 + wave + kWaves * x;
   const int wave_first = q0 + wave;
-  const bool wave_has_rows = wave_first < N;
-  const int wave_last_row = min(q0 + wave + kWaves * 31, N - 1);
+  const bool wave_has_rows = wave_first < Lq;
+  const int wave_last_row = min(q0 + wave + kWaves * 31, Lq - 1);
 
   // Q fragments (B operand of S^T = K Q^T): column x, d = 16ks + 8hi + 0..7.
   // All loads are issued before any is used (rows past the end read the last
   // row and are zeroed afterwards).
   bf16x8 qf[KS];
   {
-    const uint16_t* qr = qh + (size_t)min(qrow, N - 1) * D + hi * 8;
+    const uint16_t* qr = qh + (size_t)min(qrow, Lq - 1) * q_rs + hi * 8;
     u32x4 w[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u32x4*>(qr + ks * 16);
-    const uint32_t keep = qrow < N ? 0xffffffffu : 0u;
+    for (int kq = 0; kq < KS; ++kq) w[kq] = *reinterpret_cast<const u32x4*>(qr + kq * 16);
+    const uint32_t keep = qrow < Lq ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (w[ks] ^ qflip) & keep);
+    for (int kq = 0; kq < KS; ++kq) qf[kq] = __builtin_bit_cast(bf16x8, (w[kq] ^ qflip) & keep);
   }
 
   // ---- per-lane LDS read offsets (tile base and ks/mb/ks2 parts are immediates) ----
@@ -207,16 +227,27 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     const int p = i * kThreads + wave * 64 + lane;
     const int r = p / RC, cp = p % RC;
     dma_row[i] = r;
-    dk_off[i] = (uint32_t)(r * D * 2 + ((cp ^ k_swz<D>(r)) << 4));
-    dv_off[i] = (uint32_t)(r * D * 2 + ((cp ^ v_swz<D>(r)) << 4));
+    dk_off[i] = (uint32_t)(r * kv_rs * 2 + ((cp ^ k_swz<D>(r)) << 4));
+    dv_off[i] = (uint32_t)(r * kv_rs * 2 + ((cp ^ v_swz<D>(r)) << 4));
   }
+  f32x16 oacc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Key tiles t_begin .. t_end-1: up to the last key any row of the tile may
+  // see, from the first key of the earliest row's window.
+  const int kv_end = CAUSAL ? min(Lk, q0 + kBR + off) : Lk;
+  const int t_begin = W >= 0 ? max(0, q0 + off - W) / kBC : 0;
+  const int ntiles = max((max(kv_end, 0) + kBC - 1) / kBC - t_begin, 0);
+
   // Copy rows [k0, k0+64) of the K and V head slabs into LDS tiles.  Rows past
   // the end re-read the last row (finite values whose scores are masked).
   auto issue_tile = [&](int t, uint8_t* kl, uint8_t* vl) {
-    const int k0 = t * kBC;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * D * 2;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * D * 2;
-    if (k0 + kBC <= N) {
+    const int k0 = (t_begin + t) * kBC;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * kv_rs * 2;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * kv_rs * 2;
+    if (k0 + kBC <= Lk) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         dma16(kbase, dk_off[i], kl + (i * kThreads + wave_s * 64) * 16);
@@ -225,20 +256,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     } else {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int delta = (min(dma_row[i], N - 1 - k0) - dma_row[i]) * D * 2;
+        const int delta = (min(dma_row[i], Lk - 1 - k0) - dma_row[i]) * kv_rs * 2;
         dma16(kbase, dk_off[i] + delta, kl + (i * kThreads + wave_s * 64) * 16);
         dma16(vbase, dv_off[i] + delta, vl + (i * kThreads + wave_s * 64) * 16);
       }
     }
   };
-
-  f32x16 oacc[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
 
   // Wait until tile t+1 has landed: the tiles issued after it (up to
   // t + kStages - 1, when they exist) may stay in flight.
@@ -264,8 +287,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     }
     const uint8_t* kl = ring[t % kStages][0];
     const uint8_t* vl = ring[t % kStages][1];
-    const int k0 = t * kBC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= wave_last_row);
+    const int k0 = (t_begin + t) * kBC;
+    const bool active = wave_has_rows && (!CAUSAL || k0 <= wave_last_row + off) &&
+                        (W < 0 || k0 + kBC - 1 >= wave_first + off - W);
     if (active) {
       // ---- S^T = K Q^T : s[mb] covers keys 32mb + (8(r/4) + 4hi + r%4), query x ----
       f32x16 s[kMB];
@@ -282,13 +306,26 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
       __builtin_amdgcn_iglp_opt(0);
       // ---- mask: keys past the end, and keys after the query when causal ----
       // key = k0 + 4hi + off(mb,r), off = 32mb + 8(r/4) + r%4: masked when off > lim
-      if ((k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wave_first)) {
-        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * hi;
+      // (window: also keys before the row's window, lo = qrow + off - W)
+      if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wave_first + off) ||
+          (W >= 0 && k0 < wave_last_row + off - W)) {
+        const int lim = (CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1) - k0 - 4 * hi;
+        if (W >= 0) {
+          const int lim_lo = qrow + off - W - k0 - 4 * hi;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
+          for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
+            for (int r = 0; r < 16; ++r) {
+              const int o_ = 32 * mb + 8 * (r >> 2) + (r & 3);
+              s[mb][r] = (o_ > lim || o_ < lim_lo) ? -INFINITY : s[mb][r];
+            }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
+        }
       }
       // ---- running softmax (base 2, lazy rescale) ----
       // four independent chains of three-input maxima over the lane's scores
@@ -307,13 +344,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
       const float mxs = mx * c;  // -inf stays -inf (c > 0)
       if (__any(mxs > m_run + kTau)) {
         const float mn = fmaxf(m_run, mxs);
-        const float alpha = fast_exp2(m_run - mn);
+        // packed sequences and windows: a row may still have seen no key
+        const float alpha = (VARLEN && mn == -INFINITY) ? 1.0f : fast_exp2(m_run - mn);
         l_run *= alpha;
 #pragma unroll
         for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
         m_run = mn;
       }
-      const float negm = -m_run;
+      const float negm = (VARLEN && m_run == -INFINITY) ? 0.f : -m_run;
       float lsum[2] = {0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
@@ -366,9 +404,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   // ---- epilogue: O = O^T / l, lse = m ln2 + ln l ----
   if (!wave_has_rows) return;
   const float lt = sum_halves(l_run);
-  const float inv = 1.0f / lt;
-  if (qrow < N) {
-    uint16_t* orow = o + qbase + (size_t)qrow * D;
+  // a packed causal row with i + off < 0 (or a sequence without keys) sees no
+  // key: o = 0, lse = -inf, decided by position, not by arithmetic
+  const bool empty = VARLEN && ((CAUSAL && qrow + off < 0) || Lk == 0);
+  const float inv = empty ? 0.f : 1.0f / lt;
+  if (qrow < Lq) {
+    uint16_t* orow = o + qbase + (size_t)qrow * q_rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -376,29 +417,44 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
         const int d0 = md * 32 + 8 * g4 + 4 * hi;
         u32x2 w = {pack_bf16x2(oacc[md][4 * g4 + 0] * inv, oacc[md][4 * g4 + 1] * inv),
                    pack_bf16x2(oacc[md][4 * g4 + 2] * inv, oacc[md][4 * g4 + 3] * inv)};
+        if (empty) w = u32x2{0u, 0u};
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-    if (lse != nullptr && hi == 0) lse[(size_t)bh * N + qrow] = m_run * kLn2 + __logf(lt);
+    if (lse != nullptr && hi == 0) {
+      const float lv = empty ? -INFINITY : m_run * kLn2 + __logf(lt);
+      if (VARLEN)
+        lse[(size_t)h * vr.total_q + qstart + qrow] = lv;
+      else
+        lse[(size_t)bh * N + qrow] = lv;
+    }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const long long items = (long long)n_qtiles * a.B * a.Hq;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)items), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)items), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
-                     a.N, n_qtiles, (int)items, a.c, a.neg ? 0x80008000u : 0u);
+                     a.N, n_qtiles, (int)items, a.c, a.neg ? 0x80008000u : 0u, a.varlen);
   return hipGetLastError();
+}
+
+template <int D, bool VARLEN>
+hipError_t launch_c(const PrefillArgs& a, hipStream_t stream) {
+  return a.causal ? launch<D, true, VARLEN>(a, stream) : launch<D, false, VARLEN>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-  if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  const bool varlen = a.varlen.cu_q != nullptr;
+  if (varlen && (a.varlen.cu_k == nullptr || a.varlen.total_q <= 0 || a.varlen.total_k <= 0 || a.varlen.window < -1))
+    return hipErrorInvalidValue;
+  if (a.d == 128) return varlen ? launch_c<128, true>(a, stream) : launch_c<128, false>(a, stream);
+  if (a.d == 64) return varlen ? launch_c<64, true>(a, stream) : launch_c<64, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

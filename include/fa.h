@@ -80,6 +80,39 @@ int fa_prefill_f32(const float* q, const float* k, const float* v, float* o,
                    float scale, void* stream);
 
 /*
+ * Packed variable-length prefill: chunked prefill against a cached prefix,
+ * batches of prompts of different lengths, and a sliding (left) window.
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key /
+ * value rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.  Its n_q queries are the
+ * LAST n_q positions of its n_k keys: with off = n_k - n_q, causal row i sees
+ * keys j <= i + off (bottom-right alignment, so a chunk of new tokens sees the
+ * cached prefix and itself), and window_left = W >= 0 also drops keys
+ * j < i + off - W (-1: no window).  Each row is the same exact softmax(scale
+ * q k^T) v as fa_prefill over the keys it sees.  The retained cache a chunk
+ * attends to, and windowing as one way a runtime limits it, follow "How Does
+ * Flash Attention Reduce Memory Traffic During Local Inference?", section
+ * "Reduced IO Is Not the Same as Eliminating KV Cache"; masking, its section
+ * "Kernel Fusion Keeps More of the Attention Chain in One Execution Path".
+ *   q, o          [total_q, Hq, d]   bf16 (token-major packed rows)
+ *   k, v          [total_k, Hkv, d]  bf16
+ *   lse           [Hq, total_q]      fp32, may be NULL
+ *   cu_seqlens_q  [B+1]              int32, device memory, non-decreasing,
+ *   cu_seqlens_k  [B+1]              int32  from 0 to total_q / total_k (values
+ *                                    outside [0, total] are clamped on the
+ *                                    device: never an out-of-bounds access)
+ *   max_seqlen_q  >= every n_q (sizes the grid; rows of a longer sequence
+ *                 beyond it are not computed)
+ * A row that sees no key (causal with i + off < 0) gets o = 0, lse = -inf.
+ * Tiles outside every row's [i + off - W, i + off] range are never loaded.
+ * bf16 only; d in {64, 128}.  Work: one kernel launch on `stream`.
+ */
+int fa_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                      float* lse, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, int B, int Hq, int Hkv,
+                      int total_q, int total_k, int max_seqlen_q, int d,
+                      int causal, int window_left, float scale, void* stream);
+
+/*
  * Decode: one new query token per sequence against its KV cache.  The cache
  * grows with the context and is retained by the caller between steps; this
  * call only reads it ("How Does Flash Attention Reduce Memory Traffic ...",

@@ -157,7 +157,7 @@ def varlen_visible(i, n_q, n_k, causal, window_left):
     return lo, hi
 
 
-def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1):
+def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1, rows=None, heads=None):
     """Packed variable-length attention (chunked prefill, sliding window).
 
     q [total_q, Hq, d], k/v [total_k, Hkv, d]; sequence b owns query rows
@@ -169,7 +169,9 @@ def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1):
     Inference?", section "Reduced IO Is Not the Same as Eliminating KV
     Cache"; the masked softmax, its section "Kernel Fusion Keeps More of the
     Attention Chain in One Execution Path".  A row that sees no key gets
-    o = 0 and lse = -inf.  Returns (o [total_q, Hq, d], lse [Hq, total_q]).
+    o = 0 and lse = -inf.  `rows` (packed query rows) and `heads` restrict
+    the evaluation to those entries (the rest stay 0 / -inf).  Returns
+    (o [total_q, Hq, d], lse [Hq, total_q]).
     """
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
     total_q, hq, d = qf.shape
@@ -178,14 +180,17 @@ def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1):
     cu_k = [int(x) for x in np.asarray(cu_k).reshape(-1)]
     o = np.zeros((total_q, hq, d))
     lse = np.full((hq, total_q), -np.inf)
+    want_rows = None if rows is None else set(int(r) for r in rows)
     for b in range(len(cu_q) - 1):
         q0, n_q = cu_q[b], cu_q[b + 1] - cu_q[b]
         k0, n_k = cu_k[b], cu_k[b + 1] - cu_k[b]
-        for h in range(hq):
+        for h in (range(hq) if heads is None else heads):
             g = _kv_head(h, hq, hkv)
             kb = kf[k0:k0 + n_k, g]
             vb = vf[k0:k0 + n_k, g]
             for i in range(n_q):
+                if want_rows is not None and q0 + i not in want_rows:
+                    continue
                 lo, hi = varlen_visible(i, n_q, n_k, causal, window_left)
                 if hi < lo:
                     continue

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fa_prefill", "fa_decode", "fa_prefill_f32", "fa_decode_f32", "fa_decode_ws",
               "fa_decode_f32_ws", "fa_decode_workspace_bytes", "fa_decode_paged",
-              "fa_decode_paged_workspace_bytes", "fa_strerror", "fa_version"):
+              "fa_decode_paged_workspace_bytes", "fa_prefill_varlen", "fa_strerror", "fa_version"):
         assert n in names
     assert set(names) == set(binding.SIGNATURES)
 
@@ -148,6 +148,39 @@ def test_workspace_bytes():
     assert lib.fa_decode_workspace_bytes(0, 32, 8, 32768, 128) == 0
     assert lib.fa_decode_workspace_bytes(64, 32, 5, 32768, 128) == 0
     assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 96) == 0
+
+
+def varlen_call(fn, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cq=P, ck=P, B=2, Hq=8, Hkv=2, tq=100, tk=300, mq=60, d=128,
+             causal=1, w=-1, scale=0.1)
+    a.update(kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"],
+              a["tk"], a["mq"], a["d"], a["causal"], a["w"], ctypes.c_float(a["scale"]), None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(k=None), binding.FA_ERR_INVALID_ARG),
+    (dict(o=None), binding.FA_ERR_INVALID_ARG),
+    (dict(cq=None), binding.FA_ERR_INVALID_ARG),
+    (dict(ck=None), binding.FA_ERR_INVALID_ARG),
+    (dict(cq=ctypes.c_void_p(0x10002)), binding.FA_ERR_INVALID_ARG),
+    (dict(B=0), binding.FA_ERR_INVALID_ARG),
+    (dict(tq=0), binding.FA_ERR_INVALID_ARG),
+    (dict(tk=0), binding.FA_ERR_INVALID_ARG),
+    (dict(mq=0), binding.FA_ERR_INVALID_ARG),
+    (dict(mq=101), binding.FA_ERR_INVALID_ARG),
+    (dict(w=-2), binding.FA_ERR_INVALID_ARG),
+    (dict(causal=3), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=8, Hkv=3), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(v=P_MIS), binding.FA_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p(0x10001)), binding.FA_ERR_INVALID_ARG),
+    (dict(d=48), binding.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_varlen_rejects_invalid_arguments(kw, code):
+    assert varlen_call(binding.load_library().fa_prefill_varlen, **kw) == code
 
 
 def paged_call(fn, **kw):

@@ -3,9 +3,12 @@
 
 One step = one fa_prefill call on the causal MHA workload (B4 H32 N4096
 d128 bf16), one fa_decode call on the GQA decode workload (B64 Hq32 Hkv8 d128
-bf16, cache lengths uniform in [1024, 32768]) and one fa_decode_paged call on
-the same logical caches in 64-key pages of a shuffled pool.  Inputs are seeded
-synthetic tensors already resident in HBM before timing starts.
+bf16, cache lengths uniform in [1024, 32768]), one fa_decode_paged call on
+the same logical caches in 64-key pages of a shuffled pool, and two
+fa_prefill_varlen calls: a 4096-query chunk against a 16384-key prefix (GQA B2
+Hq32 Hkv8 d128, causal) and the MHA 4K workload with a 1024-key causal window.
+Inputs are seeded synthetic tensors already resident in HBM before timing
+starts.
 
 `value` is prefill TFLOP/s (algorithmic FLOPs = 4*d*B*Hq*(N(N+1)/2) over the
 prefill kernel's own HIP-event time); the decode figures (KV bytes read per
@@ -40,6 +43,18 @@ DECODE_SRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc", "de
 def prefill_flops(B, Hq, N, d, causal):
     pairs = N * (N + 1) // 2 if causal else N * N
     return 4 * d * B * Hq * pairs
+
+
+def varlen_pairs(lens, causal, window):
+    """Visible (query, key) pairs of packed sequences [(n_q, n_k), ...]."""
+    total = 0
+    for nq, nk in lens:
+        off = nk - nq
+        for i in range(nq):
+            hi = min(i + off, nk - 1) if causal else nk - 1
+            lo = max(0, i + off - window) if window >= 0 else 0
+            total += max(hi - lo + 1, 0)
+    return total
 
 
 def prefill_bytes(B, Hq, Hkv, N, d, elem=2):
@@ -144,7 +159,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
     ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "copy", "ceiling"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "prefill_chunked", "prefill_window",
+                                       "copy", "ceiling"], default=None,
                     help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
                          "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
                          "MFMA / HBM ceiling probes")
@@ -157,7 +173,7 @@ def main():
     import torch
 
     from exact_tiled_attention_prefill_amd import (decode, decode_paged, decode_paged_workspace_bytes,
-                                                   decode_workspace_bytes, load_library, prefill)
+                                                   decode_workspace_bytes, load_library, prefill, prefill_varlen)
     from exact_tiled_attention_prefill_amd import inputs as I
 
     load_library()  # fail loudly before any work if libfa.so is missing
@@ -178,6 +194,8 @@ def main():
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode") and not args.no_decode
     run_paged = args.only in (None, "decode_paged") and not args.no_decode
+    run_chunk = args.only in (None, "prefill_chunked")
+    run_window = args.only in (None, "prefill_window")
 
     pc = I.PREFILL_MHA_4K
     if run_prefill:
@@ -215,7 +233,33 @@ def main():
         def pgf():
             decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pod, workspace=pws)
 
+    # packed variable-length legs: a 4096-query chunk against a 16384-key prefix
+    # (GQA B2 Hq32 Hkv8 d128, causal bottom-right), and the MHA 4K workload
+    # with a 1024-key causal window
+    vl_legs = []
+    for name, on, lens, hq, hkv, causal, window in (
+            ("prefill_chunked", run_chunk, [(4096, 16384)] * 2, 32, 8, True, -1),
+            ("prefill_window", run_window, [(4096, 4096)] * 4, 32, 32, True, 1024)):
+        if not on:
+            continue
+        vq, vk, vv, cq, ck, vscale = I.varlen_inputs(lens, hq, hkv, 128, seed=5)
+        vqd, vkd, vvd, cqd, ckd = vq.to(dev), vk.to(dev), vv.to(dev), cq.to(dev), ck.to(dev)
+        vod = torch.empty_like(vqd)
+        vld = torch.empty((hq, vq.shape[0]), dtype=torch.float32, device=dev)
+        mq = max(nq for nq, _ in lens)
+
+        def vf(vqd=vqd, vkd=vkd, vvd=vvd, cqd=cqd, ckd=ckd, vod=vod, vld=vld, mq=mq, causal=causal,
+               window=window, vscale=vscale):
+            prefill_varlen(vqd, vkd, vvd, cqd, ckd, mq, causal=causal, window_left=window, scale=vscale,
+                           out=vod, lse=vld)
+        flops = 4 * 128 * hq * varlen_pairs(lens, causal, window)
+        cfg = {"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128, "causal": causal,
+               "window_left": window}
+        vl_legs.append((name, vf, flops, cfg))
+
     for _ in range(args.warmup):
+        for _, vf, _, _ in vl_legs:
+            vf()
         if run_prefill:
             pf()
         if run_decode:
@@ -226,10 +270,13 @@ def main():
 
     # timed region: K steps, each = one prefill + one decode (+ one paged decode), events per call
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 + len(vl_legs))] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        for j, (_, vf, _, _) in enumerate(vl_legs):
+            ev[i][4 + j].record(stream)
+            vf()
         ev[i][0].record(stream)
         if run_prefill:
             pf()
@@ -245,6 +292,10 @@ def main():
     p_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
     d_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
     g_ms = sorted(ev[i][2].elapsed_time(ev[i][3]) for i in range(K))
+    vl_ms = []
+    for j in range(len(vl_legs)):
+        nxt = [(4 + j + 1) if j + 1 < len(vl_legs) else 0 for _ in range(K)]
+        vl_ms.append(sorted(ev[i][4 + j].elapsed_time(ev[i][nxt[i]]) for i in range(K)))
     p_avg = sum(p_ms) / K
     d_avg = sum(d_ms) / K
     g_avg = sum(g_ms) / K
@@ -265,7 +316,8 @@ def main():
         "data": "synthetic (seeded N(0,1) rounded to bf16)",
         "config": {"workload": pc.name, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "N": pc.N, "d": pc.d,
                    "causal": pc.causal, "step": "one prefill (this workload) + one decode (decode.workload) + one paged decode "
-                                                              "(decode_paged.workload)"},
+                                                              "(decode_paged.workload) + the prefill_chunked and "
+                                                              "prefill_window legs"},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
@@ -293,6 +345,16 @@ def main():
                                          "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC)}}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
+    for (name, _, flops, cfg), ms in zip(vl_legs, vl_ms):
+        avg = sum(ms) / K
+        tf = flops / (avg * 1e-3) / 1e12
+        result[name] = {"config": cfg, "ms_avg": avg, "ms_median": ms[K // 2], "ms_min": ms[0], "tflops": tf,
+                        "flops_per_launch": flops,
+                        "roofline": {"kernel": "prefill_bf16_kernel<128,causal,varlen>", "bound": "mfma",
+                                     "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": tf / PEAK_BF16_TFLOPS}}
+        if result["value"] is None:
+            result["value"] = tf
     if run_paged:
         nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
         gbs = nbytes / (g_avg * 1e-3) / 1e9
@@ -309,10 +371,11 @@ def main():
         ceil = measured_ceilings()
         result["ceilings"] = ceil
         if ceil is not None:
-            if "roofline" in result:
-                sus = ceil["mfma_bf16_random_operands"]["tflops"]
-                result["roofline"]["measured_ceiling"] = sus
-                result["roofline"]["frac_of_measured_ceiling"] = result["roofline"]["achieved"] / sus
+            sus = ceil["mfma_bf16_random_operands"]["tflops"]
+            for rl in [result.get("roofline")] + [result[n]["roofline"] for n, _, _, _ in vl_legs]:
+                if rl is not None:
+                    rl["measured_ceiling"] = sus
+                    rl["frac_of_measured_ceiling"] = rl["achieved"] / sus
             for leg in ("decode", "decode_paged"):
                 if leg in result:
                     rl = result[leg]["roofline"]

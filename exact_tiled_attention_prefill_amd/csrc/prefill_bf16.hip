@@ -129,7 +129,8 @@ template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int Hq, int Hkv, int N, int n_qtiles, int n_items, float c, uint32_t qflip, VarlenRef vr) {
+    int Hq, int Hkv, int N, int n_qtiles, int n_items, int block_heads, float c, uint32_t qflip,
+    VarlenRef vr) {
   constexpr int KS = D / 16;                // k-steps of S^T = K Q^T
   constexpr int MD = D / 32;                // 32-row blocks of O^T
   constexpr int RC = D / 8;                 // 16-byte chunks per row
@@ -147,18 +148,29 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const int x = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: XCD-contiguous ranges, (group, tile heavy-first, head) ----
+  // ---- work item: XCD-contiguous ranges of (block of KV groups, tile
+  // heavy-first, group in the block, head).  A block holds at least
+  // block_heads query heads, so that its heaviest tiles fill an XCD's slots
+  // before lighter ones start.  Ordering heavy-first only within one MHA head
+  // would start each head's heavy tiles late, after other heads' light ones,
+  // and the XCD would finish on a long tail. ----
   int item = blockIdx.x;
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
   const int G = Hq / Hkv;
-  const int per_group = n_qtiles * G;
-  const int grp = item / per_group;  // (b, kv head)
-  const int rem = item - grp * per_group;
-  const int tslot = rem / G;
+  const int n_groups = n_items / (n_qtiles * G);  // B * Hkv
+  const int BG = G >= block_heads ? 1 : (block_heads + G - 1) / G;  // KV groups per block
+  const int per_block = BG * G * n_qtiles;
+  const int blk = item / per_block;
+  const int rem = item - blk * per_block;
+  const int gib = min(BG, n_groups - blk * BG);  // groups in this block (the last may be partial)
+  const int tslot = rem / (gib * G);
+  const int r2 = rem - tslot * gib * G;
+  const int gi = r2 / G;
+  const int grp = blk * BG + gi;  // (b, kv head)
   const int qtile = CAUSAL ? (n_qtiles - 1 - tslot) : tslot;
   const int b = grp / Hkv;
   const int g = grp - b * Hkv;
-  const int h = g * G + (rem - tslot * G);
+  const int h = g * G + (r2 - gi * G);
   const int bh = b * Hq + h;
 
   // ---- sequence geometry: Lq queries (the last Lq positions) against Lk keys;
@@ -430,15 +442,22 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   }
 }
 
+// Query heads per scheduling block: enough that a block's heaviest tiles fill
+// the ~64 workgroup slots of an XCD (4 heads below 32 query tiles per head), but
+// no more, since every head of a block streams its own K/V through the XCD's
+// L2 at the same time (measured on causal MHA d128, N 1K..16K).
+int block_heads_for(int n_qtiles) { return n_qtiles < 32 ? 4 : 2; }
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const long long items = (long long)n_qtiles * a.B * a.Hq;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int block_heads = block_heads_for(n_qtiles);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)items), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
-                     a.N, n_qtiles, (int)items, a.c, a.neg ? 0x80008000u : 0u, a.varlen);
+                     a.N, n_qtiles, (int)items, block_heads, a.c, a.neg ? 0x80008000u : 0u, a.varlen);
   return hipGetLastError();
 }
 

@@ -48,9 +48,11 @@
 //     precede a tile skips it, masks run only on diagonal and ragged tiles.
 //   * Scheduling: workgroup ids are dealt round-robin to the 8 XCDs, so each
 //     XCD is given a contiguous range of work items; within it the items are
-//     ordered (KV head group, query tile heaviest-first, query head of the
-//     group), so the query heads sharing K/V -- and neighbouring query tiles
-//     streaming the same K/V tiles -- run together on one XCD's L2.
+//     ordered (block of KV head groups, slot, group, query head of the group),
+//     so the query heads sharing K/V -- and neighbouring query tiles
+//     streaming the same K/V tiles -- run together on one XCD's L2.  Causal:
+//     a slot runs query tile n-1-s and then its mirror s, so every workgroup
+//     streams about n+1 key-tile pairs.
 #include "common.h"
 #include "kernels.h"
 
@@ -148,18 +150,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const int x = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: XCD-contiguous ranges of (block of KV groups, tile
-  // heavy-first, group in the block, head).  A block holds at least
-  // block_heads query heads, so that its heaviest tiles fill an XCD's slots
-  // before lighter ones start.  Ordering heavy-first only within one MHA head
-  // would start each head's heavy tiles late, after other heads' light ones,
-  // and the XCD would finish on a long tail. ----
+  // ---- work item: XCD-contiguous ranges of (block of KV groups, slot, group
+  // in the block, head).  A block holds at least block_heads query heads so
+  // that short sequences still spread a block over an XCD's slots. ----
   int item = blockIdx.x;
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
   const int G = Hq / Hkv;
-  const int n_groups = n_items / (n_qtiles * G);  // B * Hkv
+  // causal: slot s of a head runs query tiles n-1-s and s (equal work per slot)
+  const int n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int n_groups = n_items / (n_slots * G);  // B * Hkv
   const int BG = G >= block_heads ? 1 : (block_heads + G - 1) / G;  // KV groups per block
-  const int per_block = BG * G * n_qtiles;
+  const int per_block = BG * G * n_slots;
   const int blk = item / per_block;
   const int rem = item - blk * per_block;
   const int gib = min(BG, n_groups - blk * BG);  // groups in this block (the last may be partial)
@@ -167,7 +168,6 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const int r2 = rem - tslot * gib * G;
   const int gi = r2 / G;
   const int grp = blk * BG + gi;  // (b, kv head)
-  const int qtile = CAUSAL ? (n_qtiles - 1 - tslot) : tslot;
   const int b = grp / Hkv;
   const int g = grp - b * Hkv;
   const int h = g * G + (r2 - gi * G);
@@ -194,9 +194,20 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const uint16_t* kh = k + (VARLEN ? ((size_t)kstart * Hkv + g) * D : (size_t)grp * N * D);
   const uint16_t* vh = v + (VARLEN ? ((size_t)kstart * Hkv + g) * D : (size_t)grp * N * D);
 
+  // Causal: a slot pairs a heavy query tile with its light mirror (n-1-s, then
+  // s), so every workgroup streams about the same number of key tiles and the
+  // XCDs do not finish on a tail of long workgroups.
+  const int n_qt = VARLEN ? (Lq + kBR - 1) / kBR : n_qtiles;  // this sequence's query tiles
+  const int n_pass = CAUSAL ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+  const int qtile = !CAUSAL ? tslot : (pass == 0 ? n_qt - 1 - tslot : tslot);
+  // pass 1 only when the mirror is a different tile; past a shorter
+  // sequence's tiles the whole workgroup skips the pass
+  if (CAUSAL && (tslot > n_qt - 1 - tslot || (pass == 1 && tslot == n_qt - 1 - tslot))) continue;
+  if (VARLEN && !CAUSAL && tslot >= n_qt) continue;
+
   // Rows of this wave: q0 + wave + kWaves*j; lane column x holds row q0 + wave + kWaves*x.
   const int q0 = qtile * kBR;
-  if (VARLEN && q0 >= Lq) return;  // a shorter sequence: the whole workgroup leaves
   const int qrow = q0 + wave + kWaves * x;
   const int wave_first = q0 + wave;
   const bool wave_has_rows = wave_first < Lq;
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   for (int t = 0; t < ntiles; ++t) step(t);
 
   // ---- epilogue: O = O^T / l, lse = m ln2 + ln l ----
-  if (!wave_has_rows) return;
+  if (wave_has_rows) {
   const float lt = sum_halves(l_run);
   // a packed causal row with i + off < 0 (or a sequence without keys) sees no
   // key: o = 0, lse = -inf, decided by position, not by arithmetic
@@ -440,20 +451,24 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
         lse[(size_t)bh * N + qrow] = lv;
     }
   }
+  }  // wave_has_rows
+  }  // pass
 }
 
-// Query heads per scheduling block: enough that a block's heaviest tiles fill
-// the ~64 workgroup slots of an XCD (4 heads below 32 query tiles per head), but
-// no more, since every head of a block streams its own K/V through the XCD's
-// L2 at the same time (measured on causal MHA d128, N 1K..16K).
-int block_heads_for(int n_qtiles) { return n_qtiles < 32 ? 4 : 2; }
+// Query heads per scheduling block.  With causal tiles paired, every slot of
+// a head carries about the same work, so one head per block suffices once a
+// head has 16 or more slots; short sequences group 4 heads so that a block
+// still spans an XCD's ~64 workgroup slots (measured on causal MHA d128,
+// N 1K..16K: within 1% of the best block size at every length).
+int block_heads_for(int n_slots) { return n_slots < 16 ? 4 : 1; }
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kBR - 1) / kBR;
-  const long long items = (long long)n_qtiles * a.B * a.Hq;
+  const int n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // causal slots pair two query tiles
+  const long long items = (long long)n_slots * a.B * a.Hq;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int block_heads = block_heads_for(n_qtiles);
+  const int block_heads = block_heads_for(n_slots);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)items), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,

@@ -181,3 +181,15 @@ def varlen_inputs(lens, Hq, Hkv, d, dtype="bf16", seed=0):
     cu_q = torch.tensor([0] + [sum(nq for nq, _ in lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32)
     cu_k = torch.tensor([0] + [sum(nk for _, nk in lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32)
     return q, k, v, cu_q, cu_k, fp32_scale(d)
+
+
+def backward_inputs(B, Hq, Hkv, N, d, dtype="bf16", seed=0):
+    """(q, k, v, do, scale) for the attention backward: q, k, v as
+    prefill_inputs draws them, then the upstream gradient do [B,Hq,N,d] as
+    one more seeded N(0,1) draw rounded to bf16 (or fp32)."""
+    gen = torch.Generator().manual_seed(seed)
+    q = _draw(gen, (B, Hq, N, d), dtype)
+    k = _draw(gen, (B, Hkv, N, d), dtype)
+    v = _draw(gen, (B, Hkv, N, d), dtype)
+    do = _draw(gen, (B, Hq, N, d), dtype)
+    return q, k, v, do, fp32_scale(d)

@@ -10,7 +10,7 @@ Modules
 exact       the definition written out: materialised score matrix, softmax,
             weighted sum of values (prefill, packed variable-length prefill
             with bottom-right causal alignment and a left window, KV-cache
-            decode contiguous or paged), plus the
+            decode contiguous or paged) and its gradients, plus the
             tile-by-tile running-softmax form and the log-sum-exp merge of
             partial results that the exactness claim rests on.
 traffic     the page-1 tiled-GEMM load-count model.
@@ -22,6 +22,7 @@ scaled_dot_product_attention.
 
 from .exact import (  # noqa: F401
     attention,
+    attention_backward,
     attention_rows,
     attention_varlen,
     varlen_visible,

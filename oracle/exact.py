@@ -28,7 +28,8 @@ section):
 
 Because the fast method is exact, the reference for it is the plain
 definition (score_matrix / attention / attention_rows / decode /
-decode_paged / attention_varlen).  The running
+decode_paged / attention_varlen), and its gradients (attention_backward)
+are the chain rule through that definition.  The running
 softmax (tiled_attention) and the log-sum-exp merge (merge_partials) are
 second, independent derivations used only to pin the exactness claim and the
 split-KV merge.
@@ -201,6 +202,42 @@ def attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=-1, rows=No
                 o[q0 + i, h] = (p @ vb[lo:hi + 1]) / l
                 lse[h, q0 + i] = m + math.log(l)
     return o, lse
+
+
+def attention_backward(q, k, v, do, causal, scale):
+    """Gradients of sum(o * do) with respect to q, k and v for o = attention(q, k, v).
+
+    The probabilities are recomputed from q and k instead of being stored
+    ("11.4d FlashAttention", section "Recomputation").  For each row, with
+    p = softmax(s) over the visible keys and s = scale * q k^T:
+        dv_j += p_j do           (per visible key j)
+        dp_j  = do . v_j
+        ds_j  = p_j (dp_j - sum_j' p_j' dp_j')
+        dq   += scale * ds_j k_j,   dk_j += scale * ds_j q
+    sum_j' p_j' dp_j' equals do . o, the row's output dotted with its
+    upstream gradient.  Under GQA a key/value head's gradients sum over the
+    query heads that share it.  Returns (dq, dk, dv) in float64, shaped like
+    q, k, v.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(bsz):
+        for h in range(hq):
+            g = _kv_head(h, hq, hkv)
+            s = score_matrix(q[b, h], k[b, g], scale, causal)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            p /= p.sum(axis=1, keepdims=True)
+            dv[b, g] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, g].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, h] = float(scale) * (ds @ k[b, g])
+            dk[b, g] += float(scale) * (ds.T @ q[b, h])
+    return dq, dk, dv
 
 
 def decode(q, kcache, vcache, seqlens, scale):

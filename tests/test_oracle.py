@@ -544,3 +544,75 @@ def test_pins_catch_window_off_by_one(monkeypatch):
     q, k, v = rand((nq, 1, d), 400), rand((nk, 1, d), 401), rand((nk, 1, d), 402)
     o, _ = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], True, 0.7, window_left=0)
     assert not np.array_equal(o[1, 0], v[1 + nk - nq, 0])
+
+
+# ---------------------------------------------------------------- P24 - P26: backward
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (3, 1)])
+def test_backward_matches_torch_autograd(causal, hq, hkv):
+    """P24: dq, dk, dv equal PyTorch float64 autograd through its own
+    scaled_dot_product_attention (is_causal, enable_gqa)."""
+    g = torch.Generator().manual_seed(7 + hq + causal)
+    q = torch.randn(2, hq, 9, 5, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(2, hkv, 9, 5, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(2, hkv, 9, 5, generator=g, dtype=torch.float64, requires_grad=True)
+    do = torch.randn(2, hq, 9, 5, generator=g, dtype=torch.float64)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=0.37,
+                                                         enable_gqa=hq != hkv)
+    o.backward(do)
+    dq, dk, dv = oracle.attention_backward(q.detach(), k.detach(), v.detach(), do, causal, 0.37)
+    assert np.abs(dq - q.grad.numpy()).max() <= 1e-12
+    assert np.abs(dk - k.grad.numpy()).max() <= 1e-12
+    assert np.abs(dv - v.grad.numpy()).max() <= 1e-12
+
+
+def test_backward_matches_finite_differences():
+    """P25: central differences of sum(o * do) in float64 (step 1e-6) agree
+    with every gradient entry to 1e-7."""
+    q, k, v, do = rand((1, 2, 4, 3), 500), rand((1, 1, 4, 3), 501), rand((1, 1, 4, 3), 502), rand((1, 2, 4, 3), 503)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, True, 0.8)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention(q_, k_, v_, True, 0.8)
+        return float((o * do).sum())
+    eps = 1e-6
+    for x, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7, (which, idx, fd, grad[idx])
+
+
+def test_backward_single_key_closed_form():
+    """P26: with one visible key the softmax is constant: dq = dk = 0 and
+    dv = do (summed over the heads sharing the key/value head)."""
+    q, k, v, do = rand((1, 4, 1, 6), 510), rand((1, 2, 1, 6), 511), rand((1, 2, 1, 6), 512), rand((1, 4, 1, 6), 513)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, False, 1.3)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    assert np.allclose(dv[0, 0], do[0, 0] + do[0, 1], rtol=0, atol=1e-15)
+    assert np.allclose(dv[0, 1], do[0, 2] + do[0, 3], rtol=0, atol=1e-15)
+
+
+def test_pins_catch_missing_softmax_correction(monkeypatch):
+    """A backward that drops the -rowsum(p dp) term fails P24."""
+    def wrong(q, k, v, do, causal, scale):
+        q, k, v, do = (oatt._f64(x) for x in (q, k, v, do))
+        dq = np.zeros_like(q)
+        for h in range(q.shape[1]):
+            s = oatt.score_matrix(q[0, h], k[0, h], scale, causal)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dq[0, h] = scale * ((p * (do[0, h] @ v[0, h].T)) @ k[0, h])
+        return dq
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(1, 2, 6, 4, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(1, 2, 6, 4, generator=g, dtype=torch.float64)
+    v = torch.randn(1, 2, 6, 4, generator=g, dtype=torch.float64)
+    do = torch.randn(1, 2, 6, 4, generator=g, dtype=torch.float64)
+    torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=0.5).backward(do)
+    assert np.abs(wrong(q.detach(), k, v, do, False, 0.5) - q.grad.numpy()).max() > 1e-6

@@ -160,7 +160,7 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
     ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "prefill_chunked", "prefill_window",
-                                       "copy", "ceiling"], default=None,
+                                       "backward", "copy", "ceiling"], default=None,
                     help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
                          "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
                          "MFMA / HBM ceiling probes")
@@ -173,7 +173,8 @@ def main():
     import torch
 
     from exact_tiled_attention_prefill_amd import (decode, decode_paged, decode_paged_workspace_bytes,
-                                                   decode_workspace_bytes, load_library, prefill, prefill_varlen)
+                                                   decode_workspace_bytes, load_library, prefill, prefill_backward,
+                                                   prefill_backward_workspace_bytes, prefill_varlen)
     from exact_tiled_attention_prefill_amd import inputs as I
 
     load_library()  # fail loudly before any work if libfa.so is missing
@@ -196,6 +197,7 @@ def main():
     run_paged = args.only in (None, "decode_paged") and not args.no_decode
     run_chunk = args.only in (None, "prefill_chunked")
     run_window = args.only in (None, "prefill_window")
+    run_bwd = args.only in (None, "backward")
 
     pc = I.PREFILL_MHA_4K
     if run_prefill:
@@ -256,6 +258,21 @@ def main():
         cfg = {"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128, "causal": causal,
                "window_left": window}
         vl_legs.append((name, vf, flops, cfg))
+
+    if run_bwd:
+        # backward of the MHA 4K causal workload: the forward's o and lse feed it
+        bq, bk, bv, bdo, bscale = I.backward_inputs(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d, seed=1)
+        bqd, bkd, bvd, bdod = bq.to(dev), bk.to(dev), bv.to(dev), bdo.to(dev)
+        bo, blse = prefill(bqd, bkd, bvd, causal=True, scale=bscale)
+        bdq, bdk, bdv = torch.empty_like(bqd), torch.empty_like(bkd), torch.empty_like(bvd)
+        bws = torch.empty(prefill_backward_workspace_bytes(pc.B, pc.Hq, pc.N), dtype=torch.uint8, device=dev)
+
+        def bwf():
+            prefill_backward(bqd, bkd, bvd, bo, bdod, blse, causal=True, scale=bscale, dq=bdq, dk=bdk, dv=bdv,
+                             workspace=bws)
+        vl_legs.append(("backward", bwf, 2.5 * prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True),
+                        {"workload": pc.name, "flops": "2.5 x forward (five matrix products per score)",
+                         "kernels": "prep + dQ + dK/dV"}))
 
     for _ in range(args.warmup):
         for _, vf, _, _ in vl_legs:
@@ -350,7 +367,8 @@ def main():
         tf = flops / (avg * 1e-3) / 1e12
         result[name] = {"config": cfg, "ms_avg": avg, "ms_median": ms[K // 2], "ms_min": ms[0], "tflops": tf,
                         "flops_per_launch": flops,
-                        "roofline": {"kernel": "prefill_bf16_kernel<128,causal,varlen>", "bound": "mfma",
+                        "roofline": {"kernel": ("bwd_prep + bwd_dq + bwd_dkdv" if name == "backward"
+                                                else "prefill_bf16_kernel<128,causal,varlen>"), "bound": "mfma",
                                      "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                      "frac": tf / PEAK_BF16_TFLOPS}}
         if result["value"] is None:

@@ -16,5 +16,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     prefill,
+    prefill_backward,
+    prefill_backward_workspace_bytes,
     prefill_varlen,
 )

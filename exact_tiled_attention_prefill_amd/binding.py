@@ -33,6 +33,9 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_prefill_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                _vp]),
+    "fa_prefill_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
+                                 _vp]),
+    "fa_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
 }
@@ -285,3 +288,45 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=Fal
         int(window_left), float(scale), _stream_ptr(stream))
     _check(st, "fa_prefill_varlen")
     return (out, lse) if return_lse else out
+
+
+def prefill_backward_workspace_bytes(B, Hq, N):
+    return int(load_library().fa_prefill_backward_workspace_bytes(B, Hq, N))
+
+
+def prefill_backward(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+                     stream=None):
+    """Gradients of sum(o * dout) for o = prefill(q, k, v) (bf16).
+
+    q, o, dout [B,Hq,N,d]; k, v [B,Hkv,N,d]; lse [B,Hq,N] fp32 as returned by
+    prefill() with the same causal and scale.  Returns (dq, dk, dv).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, n, torch.bfloat16, 4)
+    _require(lse, "lse", torch.float32, 3)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v must be [B, Hkv, N, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("o/dout must match q and lse must be [B, Hq, N]")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, n, torch.bfloat16, 4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+            raise TypeError("workspace must be a uint8 device tensor")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    st = load_library().fa_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+                                            ws_ptr, ws_bytes, _stream_ptr(stream))
+    _check(st, "fa_prefill_backward")
+    return dq, dk, dv

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 PROBE_LIB = os.path.join(PKG, "libfa_probes.so")
 
-SOURCES = ["fa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["fa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "backward_bf16.hip"]
 PROBE_SOURCES = ["ceiling_probes.hip"]
 # Per-source flags.  The MFMA prefill keeps its accumulators in the VGPR form
 # of the MFMA instructions, which lets the allocator use the AGPR half of the

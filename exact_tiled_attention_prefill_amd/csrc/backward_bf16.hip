@@ -1,0 +1,547 @@
+// bf16 attention backward on gfx950 MFMA: dQ, dK, dV from Q, K, V, O, dO and
+// the forward's log-sum-exp.
+//
+// Method: the probabilities are recomputed tile by tile from Q, K and the
+// saved log-sum-exp instead of being stored ("11.4d FlashAttention", section
+// "Recomputation"); with s = scale q.k, p = exp(s - lse):
+//     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   D_i = dO_i . O_i,
+//     dQ = scale dS K,   dK = scale dS^T Q
+// (D_i is the row sum of P o dP).  Under GQA a key/value head's dK, dV sum
+// over the query heads that share it.
+//
+// Three kernels on the caller's stream:
+//   prep:  D_i and lse_i*log2(e) per query row into a workspace padded to
+//          64-row multiples (so tile copies never leave it);
+//   dQ:    one workgroup per 128 query rows (as the forward): key tiles
+//          stream through an LDS ring; per 64-key tile and wave
+//          S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T,
+//          with dS^T packed to bf16 straight from the accumulator layout
+//          into the B operand (48 MFMAs);
+//   dK/dV: one workgroup per 128 keys of one key/value head, looping over
+//          the group's query heads and their 64-row query tiles: per wave of
+//          32 keys S = Q K^T and dP = dO V^T (K, V fragments in registers),
+//          then dV += P^T dO and dK += dS^T Q with the packed P / dS as the A
+//          operand (64 MFMAs).  No atomics: every output element has one
+//          writer, so results are deterministic.
+// Q, dO (dK/dV kernel) and K (dQ kernel) are read from LDS both row-wise
+// (ds_read_b128) and transposed (ds_read_b64_tr_b16); their 16-byte chunks
+// use one XOR swizzle that leaves both access patterns free of bank
+// conflicts.
+#include "common.h"
+#include "kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBThreads = 256;  // 4 waves
+constexpr int kBQRows = 128;    // dQ kernel: query rows per workgroup
+constexpr int kBKeys = 128;     // dK/dV kernel: keys per workgroup (32 per wave)
+constexpr int kBTile = 64;      // rows per streamed K/V (dQ) or Q/dO (dK/dV) tile
+
+// Row-read swizzle (chunk ^ f(row)) for tiles only read row-wise.
+template <int D>
+__device__ __forceinline__ int swz_row(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// Swizzle for tiles read both row-wise and transposed: for rows 0..15 (the
+// 16 rows of one row read) it is a permutation, and the 4 consecutive rows of
+// a transposed read get 4 different values of its bits 2-3.
+template <int D>
+__device__ __forceinline__ int swz_both(int row) {
+  return D == 128 ? ((4 * (row & 3)) | ((row >> 2) & 3)) : ((4 * ((row >> 1) & 1)) | ((row >> 2) & 3));
+}
+
+template <int n>
+__device__ __forceinline__ void bwait_vmem_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+__device__ __forceinline__ void bbarrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// lane l's 16 bytes from base + off land at lds_wave_base + 16*l (inline asm:
+// not tracked by the compiler; completion is ordered by vmcnt + barrier)
+__device__ __forceinline__ void bdma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
+}
+// A wave-uniform pointer forced into scalar registers (the copy takes its
+// base address from SGPRs).
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+typedef short bi16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 bread_tr(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) bi16x4 lds_t;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(p)));
+}
+
+// ---------------------------------------------------------------------------
+// prep: D_i = dO_i . O_i and lse_i * log2(e); rows >= N of the padded
+// workspace get 0.  D/8 lanes per row, one 16-byte chunk each.
+template <int D>
+__global__ __launch_bounds__(kBThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                             const uint16_t* __restrict__ dout,
+                                                             const float* __restrict__ lse,
+                                                             float* __restrict__ lse2w, float* __restrict__ dw,
+                                                             int N, int Npad, long long rows) {
+  constexpr int LPR = D / 8;
+  const long long gid = (long long)blockIdx.x * kBThreads + threadIdx.x;
+  const long long prow = gid / LPR;  // padded row index over [B*H*Npad]
+  const int j = (int)(gid % LPR);
+  float acc = 0.f;
+  const long long bh = prow / Npad;
+  const int i = (int)(prow - bh * Npad);
+  const bool valid = prow < rows && i < N;
+  if (valid) {
+    const size_t off = ((size_t)bh * N + i) * D + j * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + off);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc = fmaf(bf16lo_to_f32(a[t]), bf16lo_to_f32(b[t]), acc);
+      acc = fmaf(bf16hi_to_f32(a[t]), bf16hi_to_f32(b[t]), acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (j == 0 && prow < rows) {
+    dw[prow] = valid ? acc : 0.f;
+    lse2w[prow] = valid ? lse[(size_t)bh * N + i] * kLog2e : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2w, const float* __restrict__ dw,
+    uint16_t* __restrict__ dq, int Hq, int Hkv, int N, int Npad, int n_qtiles, int n_items, float cs,
+    float scale) {
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int RC = D / 8;
+  constexpr int TILE = kBTile * D * 2;
+  constexpr int CPT = kBTile * RC / kBThreads;
+  static_assert(CPT * kBThreads == kBTile * RC, "tile must split evenly");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];  // [stage][K, V]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int x = lane & 31;
+  const int hi = lane >> 5;
+
+  int item = blockIdx.x;
+  if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
+  const int G = Hq / Hkv;
+  const int per_group = n_qtiles * G;
+  const int grp = item / per_group;
+  const int rem = item - grp * per_group;
+  const int tslot = rem / G;
+  const int qtile = CAUSAL ? (n_qtiles - 1 - tslot) : tslot;
+  const int b = grp / Hkv;
+  const int g = grp - b * Hkv;
+  const int h = g * G + (rem - tslot * G);
+  const int bh = b * Hq + h;
+  const size_t qbase = (size_t)bh * N * D;
+  const uint16_t* kh = k + (size_t)grp * N * D;
+  const uint16_t* vh = v + (size_t)grp * N * D;
+
+  const int q0 = qtile * kBQRows;
+  const int qrow = q0 + wave + 4 * x;  // rows interleaved over the waves, as in the forward
+  const int wave_first = q0 + wave;
+  const int wave_last_row = min(q0 + wave + 4 * 31, N - 1);
+  const bool wave_has_rows = wave_first < N;
+  const int qr = min(qrow, N - 1);
+
+  // Q and dO fragments: column x = row qrow, d = 16ks + 8hi + 0..7
+  bf16x8 qf[KS], df[KS];
+  {
+    const uint16_t* qp = q + qbase + (size_t)qr * D + hi * 8;
+    const uint16_t* dp = dout + qbase + (size_t)qr * D + hi * 8;
+    u32x4 wq[KS], wd[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      wq[t] = *reinterpret_cast<const u32x4*>(qp + t * 16);
+      wd[t] = *reinterpret_cast<const u32x4*>(dp + t * 16);
+    }
+    const uint32_t keep = qrow < N ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      qf[t] = __builtin_bit_cast(bf16x8, wq[t] & keep);
+      df[t] = __builtin_bit_cast(bf16x8, wd[t] & keep);
+    }
+  }
+  const float l2 = lse2w[(size_t)bh * Npad + qr];
+  const float dd = dw[(size_t)bh * Npad + qr];
+
+  // LDS read offsets.  K rows (both patterns): row x (+32mb), chunk (2ks+hi)^swz_both
+  int koff[KS], voff_r[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    koff[t] = x * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
+    voff_r[t] = x * (D * 2) + (((2 * t + hi) ^ swz_row<D>(x)) << 4);
+  }
+  // K^T transposed reads: rows 4hi + (i>>2) (+8 for the second half, +16ks2),
+  // column block md; the swizzle depends on row bits 0..3, so the +8 half
+  // has its own offset (+16 rows leave it unchanged)
+  int ktr[MD][2];
+  {
+    const int i = lane & 15;
+    const int colc = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 4 * hi + (i >> 2) + 8 * hf;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        ktr[md][hf] = row * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
+    }
+  }
+  // DMA offsets: chunk p = i*256 + tid -> row p / RC, chunk p % RC
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dk_off[CPT], dv_off[CPT];
+  int drow[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int p = i * kBThreads + wave * 64 + lane;
+    const int r = p / RC, cp = p % RC;
+    drow[i] = r;
+    dk_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_both<D>(r)) << 4));
+    dv_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_row<D>(r)) << 4));
+  }
+  auto issue = [&](int t, int st) {
+    const int k0 = t * kBTile;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * D * 2;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * D * 2;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int delta = (k0 + kBTile <= N) ? 0 : (min(drow[i], N - 1 - k0) - drow[i]) * D * 2;
+      bdma16(kb, dk_off[i] + delta, ring[st][0] + (i * kBThreads + wave_s * 64) * 16);
+      bdma16(vb, dv_off[i] + delta, ring[st][1] + (i * kBThreads + wave_s * 64) * 16);
+    }
+  };
+
+  f32x16 acc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) acc[md] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBQRows) : N;
+  const int ntiles = (kv_end + kBTile - 1) / kBTile;
+  issue(0, 0);
+  bwait_vmem_le<0>();
+  bbarrier();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    const uint8_t* kl = ring[t & 1][0];
+    const uint8_t* vl = ring[t & 1][1];
+    const int k0 = t * kBTile;
+    if (wave_has_rows && (!CAUSAL || k0 <= wave_last_row)) {
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int t2 = 0; t2 < KS; ++t2)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[t2] + mb * 32 * D * 2);
+          s[mb] = mfma32x32x16(kf, qf[t2], s[mb]);
+        }
+#pragma unroll
+      for (int t2 = 0; t2 < KS; ++t2)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + voff_r[t2] + mb * 32 * D * 2);
+          dp[mb] = mfma32x32x16(vf, df[t2], dp[mb]);
+        }
+      // key of (mb, r) = k0 + 4hi + 32mb + 8(r/4) + r%4; visible when <= lim
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool vis = 32 * mb + 8 * (r >> 2) + (r & 3) <= lim;
+          const float p = vis ? fast_exp2(fmaf(s[mb][r], cs, -l2)) : 0.f;
+          s[mb][r] = p * (dp[mb][r] - dd);  // dS^T
+        }
+#pragma unroll
+      for (int ks2 = 0; ks2 < kBTile / 16; ++ks2) {
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j];
+        const bf16x8 pf = pack_bf16x8(tmp);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const u32x2 a0 = bread_tr(kl + ktr[md][0] + (16 * ks2) * D * 2);
+          const u32x2 a1 = bread_tr(kl + ktr[md][1] + (16 * ks2) * D * 2);
+          const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+          acc[md] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf, acc[md]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) bwait_vmem_le<0>();
+    bbarrier();
+  }
+  if (wave_has_rows && qrow < N) {
+    uint16_t* orow = dq + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = md * 32 + 8 * g4 + 4 * hi;
+        u32x2 w = {pack_bf16x2(acc[md][4 * g4 + 0] * scale, acc[md][4 * g4 + 1] * scale),
+                   pack_bf16x2(acc[md][4 * g4 + 2] * scale, acc[md][4 * g4 + 3] * scale)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2w, const float* __restrict__ dw,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, int Npad, int n_kblocks,
+    int n_items, float cs, float scale) {
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int RC = D / 8;
+  constexpr int TILE = kBTile * D * 2;
+  constexpr int CPT = kBTile * RC / kBThreads;
+  static_assert(CPT * kBThreads == kBTile * RC, "tile must split evenly");
+  // [stage][Q, dO] tiles, then per stage the tile's lse2 (64 floats) and D (64 floats)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBTile];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int x = lane & 31;
+  const int hi = lane >> 5;
+
+  int item = blockIdx.x;
+  if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
+  const int grp = item / n_kblocks;           // (b, kv head)
+  const int kb = item - grp * n_kblocks;      // key block; causal: low blocks see the most queries
+  const int b = grp / Hkv;
+  const int g = grp - b * Hkv;
+  const int G = Hq / Hkv;
+  const int k0b = kb * kBKeys;
+  const int key = k0b + 32 * wave + x;        // this lane's key (column x of the wave's block)
+  const int kr = min(key, N - 1);
+  const size_t kvbase = (size_t)grp * N * D;
+
+  // K, V fragments as B operands: column x = key, d = 16ks + 8hi + 0..7
+  bf16x8 kf[KS], vf[KS];
+  {
+    const uint16_t* kp = k + kvbase + (size_t)kr * D + hi * 8;
+    const uint16_t* vp = v + kvbase + (size_t)kr * D + hi * 8;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      kf[t] = *reinterpret_cast<const bf16x8*>(kp + t * 16);
+      vf[t] = *reinterpret_cast<const bf16x8*>(vp + t * 16);
+    }
+  }
+  // LDS offsets: Q / dO rows x (+32mb) for row reads; transposed reads as in the dQ kernel
+  int roff[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) roff[t] = x * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
+  int trr[MD][2];
+  {
+    const int i = lane & 15;
+    const int colc = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 4 * hi + (i >> 2) + 8 * hf;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        trr[md][hf] = row * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
+    }
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t d_off[CPT];
+  int drow[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int p = i * kBThreads + wave * 64 + lane;
+    const int r = p / RC, cp = p % RC;
+    drow[i] = r;
+    d_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_both<D>(r)) << 4));
+  }
+
+  f32x16 dva[MD], dka[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    dva[md] = f32x16{};
+    dka[md] = f32x16{};
+  }
+
+  const int n_qt = (N + kBTile - 1) / kBTile;
+  const int qt0 = CAUSAL ? (k0b / kBTile) : 0;  // query tiles that can see this key block
+  const int per_head = n_qt - qt0;
+  const int total = per_head * G;               // (head, query tile) steps
+  // step u: head h = g*G + u / per_head, query tile qt0 + u % per_head
+  auto issue = [&](int u, int st) {
+    const int h = g * G + u / per_head;
+    const int q0 = (qt0 + u % per_head) * kBTile;
+    const size_t hb = ((size_t)b * Hq + h);
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(q + hb * N * D) + (size_t)q0 * D * 2;
+    const uint8_t* ob = reinterpret_cast<const uint8_t*>(dout + hb * N * D) + (size_t)q0 * D * 2;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int delta = (q0 + kBTile <= N) ? 0 : (min(drow[i], N - 1 - q0) - drow[i]) * D * 2;
+      bdma16(qb, d_off[i] + delta, ring[st][0] + (i * kBThreads + wave_s * 64) * 16);
+      bdma16(ob, d_off[i] + delta, ring[st][1] + (i * kBThreads + wave_s * 64) * 16);
+    }
+    // lse2 / D of the tile's 64 rows (padded workspace, always in range):
+    // waves 0-1 copy lse2, waves 2-3 copy D, 8 lanes x 16 bytes each
+    const void* src = sgpr_ptr((wave_s < 2 ? lse2w : dw) + hb * Npad + q0 + 32 * (wave_s & 1));
+    if (lane < 8)
+      bdma16(src, (uint32_t)(lane * 16), reinterpret_cast<uint8_t*>(&rowv[st][wave_s >> 1][32 * (wave_s & 1)]));
+  };
+  constexpr int DMA_PER_STEP = 2 * CPT + 1;
+
+  if (total > 0) {
+    issue(0, 0);
+    bwait_vmem_le<0>();
+    bbarrier();
+  }
+  for (int u = 0; u < total; ++u) {
+    if (u + 1 < total) issue(u + 1, (u + 1) & 1);
+    const uint8_t* ql = ring[u & 1][0];
+    const uint8_t* ol = ring[u & 1][1];
+    const float* l2t = rowv[u & 1][0];
+    const float* ddt = rowv[u & 1][1];
+    const int q0 = (qt0 + u % per_head) * kBTile;
+    // S[q, key] = Q K^T and dP[q, key] = dO V^T: rows q0 + 32mb + 8(r/4) + 4hi + r%4, column = key
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t2 = 0; t2 < KS; ++t2)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + roff[t2] + mb * 32 * D * 2);
+        s[mb] = mfma32x32x16(a, kf[t2], s[mb]);
+      }
+#pragma unroll
+    for (int t2 = 0; t2 < KS; ++t2)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + roff[t2] + mb * 32 * D * 2);
+        dp[mb] = mfma32x32x16(a, vf[t2], dp[mb]);
+      }
+    // P and dS (visible: row < N and, causal, key <= row)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 32 * mb + 8 * j + 4 * hi;  // first of the 4 rows
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2t + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ddt + rr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = q0 + rr + e;
+          const bool vis = row < N && (!CAUSAL || key <= row);
+          const float p = vis ? fast_exp2(fmaf(s[mb][4 * j + e], cs, -l4[e])) : 0.f;
+          s[mb][4 * j + e] = p;                                // P
+          dp[mb][4 * j + e] = p * (dp[mb][4 * j + e] - d4[e]);  // dS
+        }
+      }
+    // dV += P^T dO and dK += dS^T Q over four 16-row steps; the packed
+    // accumulator rows are the A operand, the transposed reads the B operand
+#pragma unroll
+    for (int ks2 = 0; ks2 < kBTile / 16; ++ks2) {
+      float tp[8], td[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j];
+        td[j] = dp[ks2 >> 1][8 * (ks2 & 1) + j];
+      }
+      const bf16x8 pa = pack_bf16x8(tp);
+      const bf16x8 da = pack_bf16x8(td);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const u32x2 o0 = bread_tr(ol + trr[md][0] + (16 * ks2) * D * 2);
+        const u32x2 o1 = bread_tr(ol + trr[md][1] + (16 * ks2) * D * 2);
+        const u32x4 ob = {o0[0], o0[1], o1[0], o1[1]};
+        dva[md] = mfma32x32x16(pa, __builtin_bit_cast(bf16x8, ob), dva[md]);
+        const u32x2 q0r = bread_tr(ql + trr[md][0] + (16 * ks2) * D * 2);
+        const u32x2 q1r = bread_tr(ql + trr[md][1] + (16 * ks2) * D * 2);
+        const u32x4 qbv = {q0r[0], q0r[1], q1r[0], q1r[1]};
+        dka[md] = mfma32x32x16(da, __builtin_bit_cast(bf16x8, qbv), dka[md]);
+      }
+    }
+    if (u + 1 < total) bwait_vmem_le<0>();
+    bbarrier();
+  }
+  (void)DMA_PER_STEP;
+
+  // dV[key][d], dK[key][d]: register r of block md holds key k0b + 32wave +
+  // 8(r/4) + 4hi + r%4 and column d = 32md + x
+  const size_t obase = kvbase;
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = k0b + 32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (kk < N) {
+        const size_t idx = obase + (size_t)kk * D + 32 * md + x;
+        dv[idx] = (uint16_t)(pack_bf16x2(dva[md][r], 0.f) & 0xffffu);
+        dk[idx] = (uint16_t)(pack_bf16x2(dka[md][r] * scale, 0.f) & 0xffffu);
+      }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
+  const int Npad = (a.N + kBTile - 1) / kBTile * kBTile;
+  float* lse2w = static_cast<float*>(a.ws);
+  float* dw = lse2w + (size_t)a.B * a.Hq * Npad;
+  const long long rows = (long long)a.B * a.Hq * Npad;
+  const long long prep_threads = rows * (D / 8);
+  const long long prep_blocks = (prep_threads + kBThreads - 1) / kBThreads;
+  if (prep_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_blocks), dim3(kBThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, lse2w, dw,
+                     a.N, Npad, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const float cs = a.scale * kLog2e;  // signed: exp2(s_raw * cs - lse * log2 e)
+  const int n_qtiles = (a.N + kBQRows - 1) / kBQRows;
+  const long long dq_items = (long long)n_qtiles * a.B * a.Hq;
+  const int n_kblocks = (a.N + kBKeys - 1) / kBKeys;
+  const long long kv_items = (long long)n_kblocks * a.B * a.Hkv;
+  if (dq_items > 0x7fffffffLL || kv_items > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)dq_items), dim3(kBThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), lse2w, dw,
+                     static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, Npad, n_qtiles, (int)dq_items, cs, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)kv_items), dim3(kBThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), lse2w, dw,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, Npad, n_kblocks,
+                     (int)kv_items, cs, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int Hq, int N) {
+  const size_t Npad = ((size_t)N + kBTile - 1) / kBTile * kBTile;
+  return 2 * (size_t)B * Hq * Npad * sizeof(float) + 256;
+}
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
+  if (a.ws_bytes < backward_workspace_bytes(a.B, a.Hq, a.N)) return hipErrorInvalidValue;
+  if (a.d == 128) return a.causal ? launch_bwd<128, true>(a, stream) : launch_bwd<128, false>(a, stream);
+  if (a.d == 64) return a.causal ? launch_bwd<64, true>(a, stream) : launch_bwd<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -186,6 +186,51 @@ int fa_prefill_varlen(const void* q, const void* k, const void* v, void* o, floa
   return fa::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_prefill_backward_workspace_bytes(int B, int Hq, int N) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return fa::backward_workspace_bytes(B, Hq, N);
+}
+
+int fa_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (N <= 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  int st = check_common(B, Hq, Hkv, d, scale);
+  if (st != FA_OK) return st;
+  const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  if (!aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Hq * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const size_t need = fa::backward_workspace_bytes(B, Hq, N);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool owned = false;
+  if (workspace != nullptr) {
+    if (workspace_bytes < need || !aligned(workspace, 256)) return FA_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != FA_OK) return st;
+  } else {
+    st = check_device();
+    if (st != FA_OK) return st;
+    if (hipMallocAsync(&workspace, need, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_NO_MEMORY;
+    }
+    owned = true;
+  }
+  fa::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal != 0, scale, workspace,
+                     owned ? need : workspace_bytes};
+  hipError_t e = fa::launch_backward_bf16(a, s);
+  if (owned) {
+    hipError_t f = hipFreeAsync(workspace, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || maxlen <= 0 || (d != 64 && d != 128) || Hq % Hkv != 0) return 0;
   return fa::decode_workspace_bytes(B, Hq, Hkv, maxlen, d);

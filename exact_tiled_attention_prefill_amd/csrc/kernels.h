@@ -66,7 +66,28 @@ struct DecodeArgs {
   PagedKV paged;   // bf16 only
 };
 
+// Backward: q, o, dout, dq [B, Hq, N, d]; k, v, dk, dv [B, Hkv, N, d] (bf16);
+// lse [B, Hq, N] fp32 (natural log, from the forward).
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;      // signed
+  void* ws;         // >= backward_workspace_bytes(B, Hq, N)
+  size_t ws_bytes;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
+size_t backward_workspace_bytes(int B, int Hq, int N);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);

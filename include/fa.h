@@ -113,6 +113,34 @@ int fa_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                       int causal, int window_left, float scale, void* stream);
 
 /*
+ * Backward of fa_prefill (bf16): gradients of sum(o * dout) with respect to
+ * q, k and v.  The attention probabilities are recomputed from q, k and the
+ * forward's log-sum-exp rather than stored ("11.4d FlashAttention", section
+ * "Recomputation"; its trade-offs section notes the extra FLOPs this costs).
+ * With p = exp(scale q.k - lse) over the visible keys of each row:
+ *     dv = p^T dout,  dp = dout v^T,  ds = p (dp - rowsum(dout * o)),
+ *     dq = scale ds k,  dk = scale ds^T q
+ * and, under GQA, a key/value head's dk, dv summed over its query heads.
+ *   q, o, dout, dq  [B, Hq, N, d]   bf16 (dq written)
+ *   k, v, dk, dv    [B, Hkv, N, d]  bf16 (dk, dv written)
+ *   lse             [B, Hq, N]      fp32: the lse fa_prefill returned for the
+ *                                   same q, k, v, causal and scale
+ * causal and scale as passed to fa_prefill; d in {64, 128}.  workspace may
+ * be NULL (obtained stream-ordered) or hold at least
+ * fa_prefill_backward_workspace_bytes(B, Hq, N) bytes, 256-byte aligned.
+ * Every output element is written by exactly one workgroup (no atomics), so
+ * the results are deterministic.  Work: three kernel launches on `stream`.
+ */
+int fa_prefill_backward(const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                        int N, int d, int causal, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_prefill_backward needs (0 if the sizes are invalid). */
+size_t fa_prefill_backward_workspace_bytes(int B, int Hq, int N);
+
+/*
  * Decode: one new query token per sequence against its KV cache.  The cache
  * grows with the context and is retained by the caller between steps; this
  * call only reads it ("How Does Flash Attention Reduce Memory Traffic ...",

@@ -151,16 +151,19 @@ def paged_cache(kcache, vcache, seqlens, page_size, seed=0, spare_pages=2):
     kp = torch.full((num_pages, Hkv, page_size, d), float("nan"), dtype=kcache.dtype, device=kcache.device)
     vp = torch.full_like(kp, float("nan"))
     table = torch.full((B, max_pages), slots[used], dtype=torch.int32)
-    j = 0
-    for b in range(B):
-        for i in range(npg[b]):
-            slot = slots[j]
-            j += 1
-            r0 = i * page_size
-            rows = min(page_size, maxlen - r0)
-            kp[slot, :, :rows] = kcache[b, :, r0:r0 + rows]
-            vp[slot, :, :rows] = vcache[b, :, r0:r0 + rows]
-            table[b, i] = slot
+    if used:
+        # logical page i of sequence b -> pool slot, all pages in one gather
+        bi = torch.tensor([b for b in range(B) for _ in range(npg[b])], dtype=torch.long)
+        pi = torch.tensor([i for b in range(B) for i in range(npg[b])], dtype=torch.long)
+        dst = torch.tensor(slots[:used], dtype=torch.long)
+        table[bi, pi] = dst.to(torch.int32)
+        pad = max_pages * page_size - maxlen  # the last page may run past maxlen: NaN rows
+        for src, pool in ((kcache, kp), (vcache, vp)):
+            if pad:
+                src = torch.cat([src, torch.full((B, Hkv, pad, d), float("nan"), dtype=src.dtype,
+                                                 device=src.device)], dim=2)
+            pages = src.reshape(B, Hkv, max_pages, page_size, d).permute(0, 2, 1, 3, 4)
+            pool[dst.to(pool.device)] = pages[bi.to(pool.device), pi.to(pool.device)]
     return kp, vp, table, num_pages
 
 

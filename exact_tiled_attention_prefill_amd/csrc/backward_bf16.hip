@@ -300,9 +300,15 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV kernel.
+// dK/dV kernel: 8 waves, two per SIMD.  Waves w and w+4 own the same 32 keys
+// (k0b + 32(w&3) + x) and split every 64-row query tile: wave w takes rows
+// 0..31, wave w+4 rows 32..63.  K fragments stay in registers; the block's
+// 128 V rows (read row-wise as the B operand of dP) are copied to LDS once.
+// The two halves' dV and dK are summed through LDS at the end.
+constexpr int kBKThreads = 512;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2w, const float* __restrict__ dw,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, int Npad, int n_kblocks,
@@ -311,45 +317,64 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
   constexpr int MD = D / 32;
   constexpr int RC = D / 8;
   constexpr int TILE = kBTile * D * 2;
-  constexpr int CPT = kBTile * RC / kBThreads;
-  static_assert(CPT * kBThreads == kBTile * RC, "tile must split evenly");
-  // [stage][Q, dO] tiles, then per stage the tile's lse2 (64 floats) and D (64 floats)
+  constexpr int CPT = kBTile * RC / kBKThreads;    // Q (and dO) chunks per thread per tile
+  constexpr int VPT = kBKeys * RC / kBKThreads;    // V-block chunks per thread
+  static_assert(CPT >= 1 && CPT * kBKThreads == kBTile * RC, "tile must split evenly");
+  static_assert(VPT * kBKThreads == kBKeys * RC, "V block must split evenly");
+  // [stage][Q, dO] tiles; at the end the ring holds the upper waves' partial sums
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t vblk[kBKeys * D * 2];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBTile];  // [stage][lse2, D][row]
+  static_assert(4 * 32 * D * 4 <= 2 * 2 * TILE, "partial sums must fit in the ring");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int x = lane & 31;
   const int hi = lane >> 5;
+  const int kw = wave & 3;    // key sub-block
+  const int half = wave >> 2;  // query rows 32*half .. +31 of every tile
 
   int item = blockIdx.x;
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
-  const int grp = item / n_kblocks;           // (b, kv head)
-  const int kb = item - grp * n_kblocks;      // key block; causal: low blocks see the most queries
+  const int grp = item / n_kblocks;       // (b, kv head)
+  const int kb = item - grp * n_kblocks;  // key block; causal: low blocks see the most queries
   const int b = grp / Hkv;
   const int g = grp - b * Hkv;
   const int G = Hq / Hkv;
   const int k0b = kb * kBKeys;
-  const int key = k0b + 32 * wave + x;        // this lane's key (column x of the wave's block)
+  const int key = k0b + 32 * kw + x;      // this lane's key (column x of the sub-block)
   const int kr = min(key, N - 1);
   const size_t kvbase = (size_t)grp * N * D;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-  // K, V fragments as B operands: column x = key, d = 16ks + 8hi + 0..7
-  bf16x8 kf[KS], vf[KS];
+  // K fragments as the B operand of S = Q K^T: column x = key, d = 16ks + 8hi + 0..7
+  bf16x8 kf[KS];
   {
     const uint16_t* kp = k + kvbase + (size_t)kr * D + hi * 8;
-    const uint16_t* vp = v + kvbase + (size_t)kr * D + hi * 8;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      kf[t] = *reinterpret_cast<const bf16x8*>(kp + t * 16);
-      vf[t] = *reinterpret_cast<const bf16x8*>(vp + t * 16);
+    for (int t = 0; t < KS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kp + t * 16);
+  }
+  // the block's V rows into LDS (rows past N re-read row N-1), swizzled for row reads
+  {
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(v + kvbase) + (size_t)k0b * D * 2;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int p = i * kBKThreads + wave * 64 + lane;
+      const int r = p / RC, cp = p % RC;
+      const int rr = min(r, N - 1 - k0b);
+      bdma16(vb, (uint32_t)(rr * D * 2 + ((cp ^ swz_row<D>(r)) << 4)), vblk + (i * kBKThreads + wave_s * 64) * 16);
     }
   }
-  // LDS offsets: Q / dO rows x (+32mb) for row reads; transposed reads as in the dQ kernel
+  int voffb[KS];  // V rows as the B operand of dP = dO V^T: row 32kw + x, chunk (2ks + hi)
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+    voffb[t] = (32 * kw + x) * (D * 2) + (((2 * t + hi) ^ swz_row<D>(x)) << 4);
+  // Q / dO rows 32*half + x for row reads; transposed reads as in the dQ kernel
   int roff[KS];
 #pragma unroll
-  for (int t = 0; t < KS; ++t) roff[t] = x * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
+  for (int t = 0; t < KS; ++t)
+    roff[t] = (32 * half + x) * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
   int trr[MD][2];
   {
     const int i = lane & 15;
@@ -359,15 +384,14 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
       const int row = 4 * hi + (i >> 2) + 8 * hf;
 #pragma unroll
       for (int md = 0; md < MD; ++md)
-        trr[md][hf] = row * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
+        trr[md][hf] = (32 * half + row) * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
     }
   }
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   uint32_t d_off[CPT];
   int drow[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int p = i * kBThreads + wave * 64 + lane;
+    const int p = i * kBKThreads + wave * 64 + lane;
     const int r = p / RC, cp = p % RC;
     drow[i] = r;
     d_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_both<D>(r)) << 4));
@@ -394,22 +418,21 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int delta = (q0 + kBTile <= N) ? 0 : (min(drow[i], N - 1 - q0) - drow[i]) * D * 2;
-      bdma16(qb, d_off[i] + delta, ring[st][0] + (i * kBThreads + wave_s * 64) * 16);
-      bdma16(ob, d_off[i] + delta, ring[st][1] + (i * kBThreads + wave_s * 64) * 16);
+      bdma16(qb, d_off[i] + delta, ring[st][0] + (i * kBKThreads + wave_s * 64) * 16);
+      bdma16(ob, d_off[i] + delta, ring[st][1] + (i * kBKThreads + wave_s * 64) * 16);
     }
     // lse2 / D of the tile's 64 rows (padded workspace, always in range):
     // waves 0-1 copy lse2, waves 2-3 copy D, 8 lanes x 16 bytes each
-    const void* src = sgpr_ptr((wave_s < 2 ? lse2w : dw) + hb * Npad + q0 + 32 * (wave_s & 1));
-    if (lane < 8)
-      bdma16(src, (uint32_t)(lane * 16), reinterpret_cast<uint8_t*>(&rowv[st][wave_s >> 1][32 * (wave_s & 1)]));
+    if (wave_s < 4) {
+      const void* src = sgpr_ptr((wave_s < 2 ? lse2w : dw) + hb * Npad + q0 + 32 * (wave_s & 1));
+      if (lane < 8)
+        bdma16(src, (uint32_t)(lane * 16), reinterpret_cast<uint8_t*>(&rowv[st][wave_s >> 1][32 * (wave_s & 1)]));
+    }
   };
-  constexpr int DMA_PER_STEP = 2 * CPT + 1;
 
-  if (total > 0) {
-    issue(0, 0);
-    bwait_vmem_le<0>();
-    bbarrier();
-  }
+  if (total > 0) issue(0, 0);
+  bwait_vmem_le<0>();  // the V block (and tile 0)
+  bbarrier();
   for (int u = 0; u < total; ++u) {
     if (u + 1 < total) issue(u + 1, (u + 1) & 1);
     const uint8_t* ql = ring[u & 1][0];
@@ -417,48 +440,42 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     const float* l2t = rowv[u & 1][0];
     const float* ddt = rowv[u & 1][1];
     const int q0 = (qt0 + u % per_head) * kBTile;
-    // S[q, key] = Q K^T and dP[q, key] = dO V^T: rows q0 + 32mb + 8(r/4) + 4hi + r%4, column = key
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    // S[q, key] = Q K^T and dP[q, key] = dO V^T over rows q0 + 32half + 8(r/4) + 4hi + r%4
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int t2 = 0; t2 < KS; ++t2)
+    for (int t2 = 0; t2 < KS; ++t2) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + roff[t2]);
+      s = mfma32x32x16(a, kf[t2], s);
+    }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + roff[t2] + mb * 32 * D * 2);
-        s[mb] = mfma32x32x16(a, kf[t2], s[mb]);
-      }
-#pragma unroll
-    for (int t2 = 0; t2 < KS; ++t2)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + roff[t2] + mb * 32 * D * 2);
-        dp[mb] = mfma32x32x16(a, vf[t2], dp[mb]);
-      }
+    for (int t2 = 0; t2 < KS; ++t2) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + roff[t2]);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vblk + voffb[t2]);
+      dp = mfma32x32x16(a, bv, dp);
+    }
     // P and dS (visible: row < N and, causal, key <= row)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 32 * half + 8 * j + 4 * hi;  // first of the 4 rows
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2t + rr);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ddt + rr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 32 * mb + 8 * j + 4 * hi;  // first of the 4 rows
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2t + rr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ddt + rr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = q0 + rr + e;
-          const bool vis = row < N && (!CAUSAL || key <= row);
-          const float p = vis ? fast_exp2(fmaf(s[mb][4 * j + e], cs, -l4[e])) : 0.f;
-          s[mb][4 * j + e] = p;                                // P
-          dp[mb][4 * j + e] = p * (dp[mb][4 * j + e] - d4[e]);  // dS
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int row = q0 + rr + e;
+        const bool vis = row < N && (!CAUSAL || key <= row);
+        const float p = vis ? fast_exp2(fmaf(s[4 * j + e], cs, -l4[e])) : 0.f;
+        s[4 * j + e] = p;                           // P
+        dp[4 * j + e] = p * (dp[4 * j + e] - d4[e]);  // dS
       }
-    // dV += P^T dO and dK += dS^T Q over four 16-row steps; the packed
-    // accumulator rows are the A operand, the transposed reads the B operand
+    }
+    // dV += P^T dO and dK += dS^T Q over two 16-row steps of the wave's rows
 #pragma unroll
-    for (int ks2 = 0; ks2 < kBTile / 16; ++ks2) {
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
       float tp[8], td[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        tp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j];
-        td[j] = dp[ks2 >> 1][8 * (ks2 & 1) + j];
+        tp[j] = s[8 * ks2 + j];
+        td[j] = dp[8 * ks2 + j];
       }
       const bf16x8 pa = pack_bf16x8(tp);
       const bf16x8 da = pack_bf16x8(td);
@@ -477,22 +494,34 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(
     if (u + 1 < total) bwait_vmem_le<0>();
     bbarrier();
   }
-  (void)DMA_PER_STEP;
 
-  // dV[key][d], dK[key][d]: register r of block md holds key k0b + 32wave +
-  // 8(r/4) + 4hi + r%4 and column d = 32md + x
-  const size_t obase = kvbase;
+  // Sum the two halves through LDS (every wave is past the last barrier, no
+  // copy is in flight), then the lower waves store.  Register r of block md
+  // holds key k0b + 32kw + 8(r/4) + 4hi + r%4 and column d = 32md + x.
+  float* red = reinterpret_cast<float*>(&ring[0][0][0]);
+  auto red_idx = [&](int md, int r) { return (kw * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * D + 32 * md + x; };
+  auto reduce_store = [&](f32x16(&acc)[MD], uint16_t* out, float mul) {
+    if (half == 1) {
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = k0b + 32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (kk < N) {
-        const size_t idx = obase + (size_t)kk * D + 32 * md + x;
-        dv[idx] = (uint16_t)(pack_bf16x2(dva[md][r], 0.f) & 0xffffu);
-        dk[idx] = (uint16_t)(pack_bf16x2(dka[md][r] * scale, 0.f) & 0xffffu);
-      }
+        for (int r = 0; r < 16; ++r) red[red_idx(md, r)] = acc[md][r];
     }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0b + 32 * kw + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float val = (acc[md][r] + red[red_idx(md, r)]) * mul;
+          if (kk < N) out[kvbase + (size_t)kk * D + 32 * md + x] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
+        }
+    }
+    __syncthreads();
+  };
+  reduce_store(dva, dv, 1.0f);
+  reduce_store(dka, dk, scale);
 }
 
 template <int D, bool CAUSAL>
@@ -522,7 +551,7 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
                      static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, Npad, n_qtiles, (int)dq_items, cs, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)kv_items), dim3(kBThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)kv_items), dim3(kBKThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), lse2w, dw,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, Npad, n_kblocks,

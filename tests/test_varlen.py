@@ -20,7 +20,9 @@ from gpu_util import BF16_LSE_MAX_ABS, check_bf16, f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MIXED = [(1, 1), (130, 130), (7, 300), (200, 1000), (64, 64), (129, 140), (50, 20), (3, 70)]
+# (n_q, n_k) per sequence: one row, ragged tiles, chunks against longer
+# prefixes, more queries than keys, and sequences without queries or keys
+MIXED = [(1, 1), (130, 130), (7, 300), (200, 1000), (0, 5), (64, 64), (129, 140), (50, 20), (5, 0), (3, 70)]
 
 
 def run_varlen(q, k, v, cu_q, cu_k, causal, window, scale):

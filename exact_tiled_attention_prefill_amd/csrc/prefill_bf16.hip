@@ -32,20 +32,24 @@
 //     be permuted freely as long as V^T uses the same order), so P never
 //     touches LDS, and O^T keeps each query's output in its own lane.
 //   * K and V tiles (64 keys) are copied HBM -> LDS by global_load_lds_dwordx4
-//     (no VGPR staging) into a ring of LDS stages (two by default: the next
-//     tile streams in while the current one is computed; the ring depth, tile
-//     size and waves per workgroup are compile-time parameters -- deeper
-//     rings and 8-wave workgroups were measured slower on MI355X).  The
+//     (no VGPR staging) into a two-slot ring: K of the tile after next and V
+//     of the next tile stream in while the current ones are read.  The
 //     workgroup barrier between tiles does not drain in-flight DMA.  K is read
-//     with ds_read_b128, V with
-//     the gfx950 transposing ds_read_b64_tr_b16 straight into the MFMA A
-//     operand layout.  16-byte chunks are XOR-swizzled by row so both reads
-//     are bank-conflict free; the DMA source addresses apply the same swizzle.
+//     with ds_read_b128, V with the gfx950 transposing ds_read_b64_tr_b16
+//     straight into the MFMA A operand layout.  16-byte chunks are
+//     XOR-swizzled by row so both reads are bank-conflict free; the DMA source
+//     addresses apply the same swizzle.
+//   * Software pipeline inside each wave: while the matrix cores compute the
+//     scores of tile t+1, the VALU turns the scores of tile t into
+//     probabilities; while the V-side products of tile t run, the VALU takes
+//     the row max of tile t+1.  Scheduling-group hints interleave the two
+//     instruction streams, and the ring slots are compile-time constants (the
+//     loop is unrolled by two), so no address arithmetic runs per tile.
 //   * The running max is updated lazily: the output is rescaled only when a
 //     row max grows by more than 2^8; otherwise exponents are taken against
 //     the stale max (p <= 256; exact after the final division by l).
-//   * Causal: tiles above the diagonal are never loaded, a wave whose rows all
-//     precede a tile skips it, masks run only on diagonal and ragged tiles.
+//   * Causal: tiles above the diagonal are never loaded; masks run only on
+//     diagonal, ragged and window tiles.
 //   * Scheduling: workgroup ids are dealt round-robin to the 8 XCDs, so each
 //     XCD is given a contiguous range of work items; within it the items are
 //     ordered (block of KV head groups, slot, group, query head of the group),
@@ -55,26 +59,26 @@
 //     streams about n+1 key-tile pairs.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace fa {
 namespace {
 
-// Launch shape (compile-time): waves per workgroup, keys per tile, ring depth.
+// Launch shape (compile-time): waves per workgroup and keys per tile.  Eight
+// waves (256 query rows sharing each K/V tile) halve the L2 -> LDS traffic and
+// run 3-5% faster from 8K keys on, but lose at 1K-4K, where one workgroup per
+// CU leaves its prologue and the wider causal diagonal exposed.
 #ifndef FA_PREFILL_WAVES
 #define FA_PREFILL_WAVES 4
 #endif
 #ifndef FA_PREFILL_BC
 #define FA_PREFILL_BC 64
 #endif
-#ifndef FA_PREFILL_STAGES
-#define FA_PREFILL_STAGES 2
-#endif
 constexpr int kWaves = FA_PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;       // query rows per workgroup
 constexpr int kBC = FA_PREFILL_BC;     // keys per tile (32 or 64)
 constexpr int kMB = kBC / 32;          // 32-key MFMA blocks per tile
-constexpr int kStages = FA_PREFILL_STAGES;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // Chunk swizzles (16-byte chunks within a tile row of D/8 chunks).
@@ -96,10 +100,9 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 // Workgroup barrier that does not drain the DMA ring.  The caller has
-// already waited (vmcnt) for the tile the next step reads, and every LDS
-// read issued so far has been consumed, so only the s_barrier itself is
-// needed; the empty asm statements keep the compiler from moving memory
-// operations across it.
+// already waited (vmcnt) for the tiles the next step reads and (lgkmcnt) for
+// its own LDS reads, so only the s_barrier itself is needed; the empty asm
+// statements keep the compiler from moving memory operations across it.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -138,11 +141,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   constexpr int RC = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = kBC * D * 2;         // bytes per K (or V) tile
   constexpr int CPT = kBC * RC / kThreads;  // DMA chunks per thread per K (or V) tile
-  constexpr int DMA_PER_TILE = 2 * CPT;     // vector-memory ops per thread per tile
   static_assert(CPT * kThreads == kBC * RC, "tile must split evenly");
-  // Ring of kStages K/V tile pairs.  The DMA into the ring is inline asm, so
-  // the compiler does not track it; ordering is explicit (vmcnt + barrier).
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][2][TILE];
+  // Two ring slots of K and V tiles: ring[slot][0] = K, ring[slot][1] = V.
+  // The DMA into the ring is inline asm, so the compiler does not track it;
+  // ordering is explicit (vmcnt + lgkmcnt + barrier).
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -228,14 +231,20 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   }
 
   // ---- per-lane LDS read offsets (tile base and ks/mb/ks2 parts are immediates) ----
+  // They are derived from a copy of the lane id taken inside the pass, so the
+  // compiler recomputes them per pass instead of keeping them live (and
+  // spilled) across the whole kernel.
+  int lp;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(lp) : "v"(lane));
+  const int xp = lp & 31, hp = lp >> 5;
   int koff[KS];  // K: row x (+32 mb), chunk (2ks + hi) swizzled
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = x * (D * 2) + (((2 * ks + hi) ^ k_swz<D>(x)) << 4);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = xp * (D * 2) + (((2 * ks + hp) ^ k_swz<D>(xp)) << 4);
   int voff[MD];  // V^T fragments: row 4hi + (i>>2) (+16ks2 + 8half), chunk of column md*32 + ...
   {
-    const int i = lane & 15;
-    const int row = 4 * hi + (i >> 2);
-    const int colc = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);  // chunk within the 32-column block
+    const int i = lp & 15;
+    const int row = 4 * hp + (i >> 2);
+    const int colc = 2 * ((lp >> 4) & 1) + ((i & 3) >> 1);  // chunk within the 32-column block
 #pragma unroll
     for (int md = 0; md < MD; ++md)
       voff[md] = row * (D * 2) + (((4 * md + colc) ^ v_swz<D>(row)) << 4) + 8 * (i & 1);
@@ -243,16 +252,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
 
   // ---- DMA: chunk p = i*kThreads + wave*64 + lane of the tile; byte offsets within the tile ----
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar: LDS bases go to M0 directly
-  uint32_t dk_off[CPT], dv_off[CPT];
-  int dma_row[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int p = i * kThreads + wave * 64 + lane;
-    const int r = p / RC, cp = p % RC;
-    dma_row[i] = r;
-    dk_off[i] = (uint32_t)(r * kv_rs * 2 + ((cp ^ k_swz<D>(r)) << 4));
-    dv_off[i] = (uint32_t)(r * kv_rs * 2 + ((cp ^ v_swz<D>(r)) << 4));
-  }
+  // rows of chunk i are dma_row + i*kRowStep; the swizzle depends on the row
+  // only modulo 16, so one offset serves every chunk of a lane
+  constexpr int kRowStep = kThreads / RC;
+  static_assert(kRowStep % 16 == 0, "row step keeps the swizzle");
+  const int dma_row = (wave * 64 + lp) / RC;
+  const int dma_cp = lp % RC;
+  const uint32_t dk_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ k_swz<D>(dma_row)) << 4));
+  const uint32_t dv_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ v_swz<D>(dma_row)) << 4));
   f32x16 oacc[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
@@ -264,107 +271,108 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
   const int t_begin = W >= 0 ? max(0, q0 + off - W) / kBC : 0;
   const int ntiles = max((max(kv_end, 0) + kBC - 1) / kBC - t_begin, 0);
 
-  // Copy rows [k0, k0+64) of the K and V head slabs into LDS tiles.  Rows past
-  // the end re-read the last row (finite values whose scores are masked).
-  auto issue_tile = [&](int t, uint8_t* kl, uint8_t* vl) {
+  // Copy rows [k0, k0+64) of the K (IS_K) or V head slab into an LDS tile.
+  // Rows past the end re-read the last row (finite values whose scores are
+  // masked).
+  auto issue_half = [&](int t, auto is_k, uint8_t* lds) {
+    constexpr bool IS_K = decltype(is_k)::value;
     const int k0 = (t_begin + t) * kBC;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * kv_rs * 2;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * kv_rs * 2;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(IS_K ? kh : vh) + (size_t)k0 * kv_rs * 2;
+    const uint32_t doff = IS_K ? dk_off : dv_off;
     if (k0 + kBC <= Lk) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        dma16(kbase, dk_off[i], kl + (i * kThreads + wave_s * 64) * 16);
-        dma16(vbase, dv_off[i], vl + (i * kThreads + wave_s * 64) * 16);
-      }
+      for (int i = 0; i < CPT; ++i)
+        dma16(base + (size_t)i * kRowStep * kv_rs * 2, doff, lds + (i * kThreads + wave_s * 64) * 16);
     } else {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int delta = (min(dma_row[i], Lk - 1 - k0) - dma_row[i]) * kv_rs * 2;
-        dma16(kbase, dk_off[i] + delta, kl + (i * kThreads + wave_s * 64) * 16);
-        dma16(vbase, dv_off[i] + delta, vl + (i * kThreads + wave_s * 64) * 16);
+        // offset from the tile base: the clamped row is >= 0, so the unsigned
+        // 32-bit offset never wraps
+        const int r = min(dma_row + i * kRowStep, Lk - 1 - k0);
+        dma16(base, doff + (r - dma_row) * kv_rs * 2, lds + (i * kThreads + wave_s * 64) * 16);
       }
     }
   };
 
-  // Wait until tile t+1 has landed: the tiles issued after it (up to
-  // t + kStages - 1, when they exist) may stay in flight.
-  auto wait_next = [&](int t) {
-    const int after = min(kStages - 2, ntiles - 2 - t);
-    static_assert(kStages >= 2 && kStages <= 5, "ring depth");
-    if (kStages >= 5 && after >= 3)
-      wait_vmem_le<3 * DMA_PER_TILE>();
-    else if (kStages >= 4 && after >= 2)
-      wait_vmem_le<2 * DMA_PER_TILE>();
-    else if (kStages >= 3 && after >= 1)
-      wait_vmem_le<DMA_PER_TILE>();
-    else
-      wait_vmem_le<0>();
+  // Keys past the end, after the query (causal) or before its window: only
+  // diagonal, ragged and window tiles need the mask.
+  auto needs_mask = [&](int k0) {
+    return (k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wave_first + off) ||
+           (W >= 0 && k0 < wave_last_row + off - W);
   };
-
-  // One tile step: compute tile t from its ring slot while tile t + kStages - 1
-  // streams into the slot freed by tile t - 1.
-  auto step = [&](int t) {
-    if (t + kStages - 1 < ntiles) {
-      const int ns = (t + kStages - 1) % kStages;
-      issue_tile(t + kStages - 1, ring[ns][0], ring[ns][1]);
+  // key = k0 + 4hi + o, o = 32mb + 8(r/4) + r%4: masked when o > lim (or o < lim_lo)
+  auto mask_scores = [&](f32x16 (&s)[kMB], int k0) {
+    const int lim = (CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1) - k0 - 4 * hi;
+    if (W >= 0) {
+      const int lim_lo = qrow + off - W - k0 - 4 * hi;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o_ = 32 * mb + 8 * (r >> 2) + (r & 3);
+          s[mb][r] = (o_ > lim || o_ < lim_lo) ? -INFINITY : s[mb][r];
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
     }
-    const uint8_t* kl = ring[t % kStages][0];
-    const uint8_t* vl = ring[t % kStages][1];
-    const int k0 = (t_begin + t) * kBC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= wave_last_row + off) &&
-                        (W < 0 || k0 + kBC - 1 >= wave_first + off - W);
-    if (active) {
-      // ---- S^T = K Q^T : s[mb] covers keys 32mb + (8(r/4) + 4hi + r%4), query x ----
-      f32x16 s[kMB];
+  };
+  // Row max of a score tile: four independent chains of three-input maxima
+  // over the lane's scores, then the other half-wave's.
+  auto rowmax = [&](const f32x16 (&s)[kMB]) {
+    float m4[4];
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) s[mb] = f32x16{};
+    for (int j = 0; j < 4; ++j) {
+      constexpr int per = 16 * kMB / 4;
+      const int e0 = j * per;
+      float m = fmaxf(s[e0 >> 4][e0 & 15], s[(e0 + 1) >> 4][(e0 + 1) & 15]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int e = e0 + 2; e + 1 < e0 + per; e += 2)
+        m = fmaxf(fmaxf(m, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
+      m4[j] = m;
+    }
+    return max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  };
+  // S^T = K Q^T for one tile: s[mb] covers keys 32mb + (8(r/4) + 4hi + r%4), query x
+  auto scores = [&](f32x16 (&s)[kMB], const uint8_t* kl) {
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[ks] + mb * 32 * D * 2);
-          s[mb] = mfma32x32x16(kf, qf[ks], s[mb]);
-        }
-      // let the scheduler interleave the K fragment reads with the MFMAs
-      __builtin_amdgcn_iglp_opt(0);
-      // ---- mask: keys past the end, and keys after the query when causal ----
-      // key = k0 + 4hi + off(mb,r), off = 32mb + 8(r/4) + r%4: masked when off > lim
-      // (window: also keys before the row's window, lo = qrow + off - W)
-      if ((k0 + kBC > Lk) || (CAUSAL && k0 + kBC - 1 > wave_first + off) ||
-          (W >= 0 && k0 < wave_last_row + off - W)) {
-        const int lim = (CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1) - k0 - 4 * hi;
-        if (W >= 0) {
-          const int lim_lo = qrow + off - W - k0 - 4 * hi;
+    for (int mb = 0; mb < kMB; ++mb) s[mb] = f32x16{};
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int o_ = 32 * mb + 8 * (r >> 2) + (r & 3);
-              s[mb][r] = (o_ > lim || o_ < lim_lo) ? -INFINITY : s[mb][r];
-            }
-        } else {
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s[mb][r] = (32 * mb + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[mb][r];
-        }
+      for (int mb = 0; mb < kMB; ++mb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + koff[ks] + mb * 32 * D * 2);
+        s[mb] = mfma32x32x16(kf, qf[ks], s[mb]);
       }
-      // ---- running softmax (base 2, lazy rescale) ----
-      // four independent chains of three-input maxima over the lane's scores
-      float m4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        constexpr int per = 16 * kMB / 4;  // scores per chain
-        const int e0 = j * per;
-        float m = fmaxf(s[e0 >> 4][e0 & 15], s[(e0 + 1) >> 4][(e0 + 1) & 15]);
-#pragma unroll
-        for (int e = e0 + 2; e + 1 < e0 + per; e += 2)
-          m = fmaxf(fmaxf(m, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
-        m4[j] = m;
-      }
-      float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-      const float mxs = mx * c;  // -inf stays -inf (c > 0)
+  };
+  // Every LDS read of this wave has returned (so a slot may be refilled
+  // after the following barrier).
+  auto lds_reads_done = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+
+  // Software pipeline over key tiles: iteration t finishes tile t (its
+  // probabilities and O^T += V^T P^T) while the matrix cores already compute
+  // the scores of tile t+1, and takes the row max of tile t+1 while the
+  // V-side products of tile t run.  Ring slot t%2 holds K(t) and V(t); during
+  // iteration t, K(t+2) and V(t+1) stream into the slots that tiles t (K) and
+  // t-1 (V) no longer need.
+  // Score tiles alternate between two register sets (no copies): iteration t
+  // finishes sc (tile t) and fills sn (tile t+1); mx_c / mx_n are their row
+  // maxima (unscaled).
+  f32x16 sA[kMB], sB[kMB];
+  float mxA = -INFINITY, mxB = -INFINITY;
+
+  auto iter = [&](int t, f32x16 (&sc)[kMB], f32x16 (&sn)[kMB], float& mx_c, float& mx_n, auto slot_c,
+                  auto full_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr bool FULL = decltype(full_c)::value;  // tile t+1 exists
+    if (t + 2 < ntiles) issue_half(t + 2, std::true_type{}, ring[SL][0]);
+    if (t + 1 < ntiles) issue_half(t + 1, std::false_type{}, ring[SL ^ 1][1]);
+    // lazy rescale against tile t's row max
+    {
+      const float mxs = mx_c * c;  // -inf stays -inf (c > 0)
       if (__any(mxs > m_run + kTau)) {
         const float mn = fmaxf(m_run, mxs);
         // packed sequences and windows: a row may still have seen no key
@@ -374,55 +382,97 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
         for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
         m_run = mn;
       }
-      const float negm = (VARLEN && m_run == -INFINITY) ? 0.f : -m_run;
+    }
+    const float negm = (VARLEN && m_run == -INFINITY) ? 0.f : -m_run;
+    // ---- region A: scores of tile t+1 || probabilities of tile t ----
+    if constexpr (FULL) scores(sn, ring[SL ^ 1][0]);
+    bf16x8 pf[kBC / 16];
+    {
       float lsum[2] = {0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[mb][r], c, negm));
-          s[mb][r] = p;
+          const float p = fast_exp2(fmaf(sc[mb][r], c, negm));
+          sc[mb][r] = p;
           lsum[r & 1] += p;
         }
       l_run += lsum[0] + lsum[1];
-      // ---- O^T += V^T P^T over four 16-key steps ----
 #pragma unroll
       for (int ks2 = 0; ks2 < kBC / 16; ++ks2) {
         float tmp[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j];
-        const bf16x8 pf = pack_bf16x8(tmp);
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const u32x2 a0 = ds_read_tr(vl + voff[md] + (16 * ks2) * D * 2);
-          const u32x2 a1 = ds_read_tr(vl + voff[md] + (16 * ks2 + 8) * D * 2);
-          const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-          oacc[md] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf, oacc[md]);
-        }
+        for (int j = 0; j < 8; ++j) tmp[j] = sc[ks2 >> 1][8 * (ks2 & 1) + j];
+        pf[ks2] = pack_bf16x8(tmp);
       }
     }
-    __builtin_amdgcn_iglp_opt(0);
-    if (t + 1 < ntiles) wait_next(t);
+    if constexpr (FULL) {
+      // one K-fragment read and about seven VALU ops per matrix product
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < KS * kMB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        if (i + 2 < KS * kMB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      // keep the probabilities in this block: without a use here the
+      // compiler sinks them past the mask branch, next to their products
+#pragma unroll
+      for (int ks2 = 0; ks2 < kBC / 16; ++ks2) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[ks2])));
+      asm volatile("" ::"v"(l_run));
+      const int k1 = (t_begin + t + 1) * kBC;
+      if (needs_mask(k1)) mask_scores(sn, k1);
+    }
+    // ---- region B: O^T += V^T P^T for tile t || row max of tile t+1 ----
+    const uint8_t* vl = ring[SL][1];
+#pragma unroll
+    for (int ks2 = 0; ks2 < kBC / 16; ++ks2)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const u32x2 a0 = ds_read_tr(vl + voff[md] + (16 * ks2) * D * 2);
+        const u32x2 a1 = ds_read_tr(vl + voff[md] + (16 * ks2 + 8) * D * 2);
+        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+        oacc[md] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf[ks2], oacc[md]);
+      }
+    if constexpr (FULL) {
+      mx_n = rowmax(sn);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < MD * kBC / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        if (i + 2 < MD * kBC / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+    if (t + 1 < ntiles) wait_vmem_le<0>();
+    lds_reads_done();
     ring_barrier();
   };
 
-  // prologue: tiles 0 .. kStages-2 in flight; wait for tile 0
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < ntiles) issue_tile(t, ring[t][0], ring[t][1]);
-  {
-    const int after = min(kStages - 2, ntiles - 1);
-    if (kStages >= 5 && after >= 3)
-      wait_vmem_le<3 * DMA_PER_TILE>();
-    else if (kStages >= 4 && after >= 2)
-      wait_vmem_le<2 * DMA_PER_TILE>();
-    else if (kStages >= 3 && after >= 1)
-      wait_vmem_le<DMA_PER_TILE>();
-    else
-      wait_vmem_le<0>();
+  if (ntiles > 0) {
+    // prologue: K(0), V(0) and K(1) in flight; scores and row max of tile 0
+    issue_half(0, std::true_type{}, ring[0][0]);
+    issue_half(0, std::false_type{}, ring[0][1]);
+    if (ntiles > 1) issue_half(1, std::true_type{}, ring[1][0]);
+    wait_vmem_le<0>();
+    ring_barrier();
+    scores(sA, ring[0][0]);
+    if (needs_mask(t_begin * kBC)) mask_scores(sA, t_begin * kBC);
+    mxA = rowmax(sA);
+    lds_reads_done();
+    ring_barrier();  // K(0)'s slot is refilled by iteration 0
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::true_type{});
+      iter(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{}, std::true_type{});
+    }
+    if (t + 1 < ntiles) {
+      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::true_type{});
+      iter(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{}, std::false_type{});
+    } else {
+      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::false_type{});
+    }
   }
-  ring_barrier();
-  for (int t = 0; t < ntiles; ++t) step(t);
 
   // ---- epilogue: O = O^T / l, lse = m ln2 + ln l ----
   if (wave_has_rows) {

@@ -88,6 +88,25 @@ def measured_traffic(name, src):
     return float(m.group(1))
 
 
+def measured_counters(name, src, keys):
+    """Derived rocprofv3 counter figures (MFMA busy fraction, counted MFMA
+    FLOPs over algorithmic FLOPs, clock, HBM rate) from a committed summary,
+    used only while the kernel source still has the summary's hash."""
+    path = os.path.join(PROFILES, name + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    if not h or h.group(1) != source_hash(src):
+        return None
+    out = {}
+    for key in keys:
+        m = re.search(key + r":\s*([0-9.eE+-]+)", text)
+        if m:
+            out[key] = float(m.group(1))
+    return out or None
+
+
 def measured_ceilings():
     """Sustained MFMA and HBM-read rates of this device from libfa_probes.so.
 
@@ -120,6 +139,24 @@ def measured_ceilings():
     out["note"] = ("whole-chip sustained v_mfma_f32_32x32x16_bf16 rate (two waves per SIMD, operands in "
                    "registers) and 4 GiB read-only stream with 16-byte loads")
     return out
+
+
+def device_memory(fn, io, workspace, n_by_n):
+    """Device bytes around one call: the call's inputs and outputs, the
+    caller-owned workspace it is given, torch's peak over the call (the
+    library allocates nothing of its own on these paths), and what an N x N
+    fp32 score buffer would take."""
+    import torch
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    fn()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    return {"io_bytes": sum(t.numel() * t.element_size() for t in io), "workspace_bytes": workspace,
+            "allocated_before_call": before, "peak_during_call": peak,
+            "extra_over_call": peak - before, "n_by_n_fp32_scores_bytes": n_by_n}
 
 
 def cpu_baseline(q, k, v, scale, seconds):
@@ -208,6 +245,8 @@ def main():
 
         def pf():
             prefill(qd, kd, vd, causal=True, scale=scale, out=od, lse=lsed)
+        p_mem = device_memory(pf, [qd, kd, vd, od, lsed], 0,
+                              pc.B * pc.Hq * pc.N * pc.N * 4)
 
     dc = I.DECODE_GQA
     if run_decode or run_paged:
@@ -222,6 +261,7 @@ def main():
 
         def df():
             decode(dqd, dkd, dvd, dld, scale=dscale, out=dod, workspace=ws)
+        d_mem = device_memory(df, [dqd, dkd, dvd, dld, dod], ws.numel(), None)
     if run_paged:
         # the same logical caches scattered over a shuffled pool of pages
         kpd, vpd, table, _ = I.paged_cache(dkd, dvd, dl, args.page_size, seed=11)
@@ -349,7 +389,11 @@ def main():
         result["roofline"] = {"kernel": "prefill_bf16_kernel<128,causal>", "bound": "mfma",
                               "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                              "algorithmic_bytes": prefill_bytes(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d)}
+                              "algorithmic_bytes": prefill_bytes(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d),
+                              "rocprof": measured_counters("prefill_bf16_mha4k_counters", PREFILL_SRC,
+                                                           ("mfma_busy_fraction", "mfma_flops_over_algorithmic",
+                                                            "shader_clock_ghz"))}
+        result["prefill"]["device_memory"] = p_mem
     if run_decode:
         nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d)
         gbs = nbytes / (d_avg * 1e-3) / 1e9
@@ -359,7 +403,10 @@ def main():
                             "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel",
                                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                         "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC)}}
+                                         "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
+                                         "rocprof": measured_counters("decode_gqa_counters", DECODE_SRC,
+                                                                      ("hbm_gbs_counter_run", "shader_clock_ghz"))},
+                            "device_memory": d_mem}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
     for (name, _, flops, cfg), ms in zip(vl_legs, vl_ms):

@@ -159,8 +159,12 @@ def device_memory(fn, io, workspace, n_by_n):
             "extra_over_call": peak - before, "n_by_n_fp32_scores_bytes": n_by_n}
 
 
-def cpu_baseline(q, k, v, scale, seconds):
-    """Time the fp64 oracle on sampled causal rows of the prefill workload."""
+def cpu_baseline(q, k, v, scale, seconds, o_gpu=None, lse_gpu=None):
+    """Time the fp64 oracle on sampled causal rows of the prefill workload.
+
+    When the GPU's output (host copies) is given, the same oracle rows also
+    give the error of those rows: max-abs / mean-abs of O and max-abs of lse.
+    """
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -171,19 +175,34 @@ def cpu_baseline(q, k, v, scale, seconds):
     rows = sample_rows(N, 2048, seed=3)  # ~2100 rows spread over the sequence, per head
     heads = [(b, h) for b in range(B) for h in range(Hq)]
     done_flops, done_rows, done_heads, t0 = 0, 0, 0, time.perf_counter()
+    err = {"o_max_abs": 0.0, "o_abs_sum": 0.0, "o_count": 0, "lse_max_abs": 0.0}
     with threadpool_limits(limits=1):
         for b, h in heads:
-            oracle.attention_rows(q, k, v, True, scale, rows, [(b, h)])
+            ro, rl = oracle.attention_rows(q, k, v, True, scale, rows, [(b, h)])
             done_flops += sum(4 * d * (r + 1) for r in rows)
             done_rows += len(rows)
             done_heads += 1
+            if o_gpu is not None:
+                e = np.abs(o_gpu[b, h, rows].double().numpy() - ro[0])
+                err["o_max_abs"] = max(err["o_max_abs"], float(e.max()))
+                err["o_abs_sum"] += float(e.sum())
+                err["o_count"] += e.size
+                el = np.abs(lse_gpu[b, h, rows].double().numpy() - rl[0])
+                err["lse_max_abs"] = max(err["lse_max_abs"], float(el.max()))
             if time.perf_counter() - t0 >= seconds:
                 break
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_rows} causal query rows ({len(rows)} sampled rows x {done_heads} heads) of "
-                      f"the B4 H32 N4096 d128 workload, fp64 numpy, {dt:.1f} s, 1 BLAS thread; "
-                      f"the rate is algorithmic FLOPs of those rows over wall time"}
+    out = {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done_rows} causal query rows ({len(rows)} sampled rows x {done_heads} heads) of "
+                     f"the B4 H32 N4096 d128 workload, fp64 numpy, {dt:.1f} s, 1 BLAS thread; "
+                     f"the rate is algorithmic FLOPs of those rows over wall time"}
+    if o_gpu is not None and err["o_count"]:
+        mean = err["o_abs_sum"] / err["o_count"]
+        out["gpu_error_on_these_rows"] = {
+            "o_max_abs": err["o_max_abs"], "o_mean_abs": mean, "lse_max_abs": err["lse_max_abs"],
+            "bar": {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3},
+            "within_bar": err["o_max_abs"] <= 2e-2 and mean <= 2e-3 and err["lse_max_abs"] <= 1e-3}
+    return out
 
 
 def main():
@@ -376,7 +395,8 @@ def main():
                                                               "(decode_paged.workload) + the prefill_chunked and "
                                                               "prefill_window legs"},
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None)},
     }
     if run_prefill:
         F = prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True)
@@ -447,7 +467,7 @@ def main():
                     rl["measured_ceiling"] = ceil["hbm_read_gbs"]
                     rl["frac_of_measured_ceiling"] = rl["achieved"] / ceil["hbm_read_gbs"]
     if run_prefill and not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds, od.cpu(), lsed.cpu())
     print(json.dumps(result), flush=True)
 
 

@@ -124,20 +124,26 @@ def measured_ceilings():
     lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double)]
     lib.fa_probe_mfma_bf16.restype = ctypes.c_int
-    lib.fa_probe_hbm_read.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
-    lib.fa_probe_hbm_read.restype = ctypes.c_int
+    lib.fa_probe_hbm_read_hint.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_double)]
+    lib.fa_probe_hbm_read_hint.restype = ctypes.c_int
     out = {}
     for name, zero in (("mfma_bf16_random_operands", 0), ("mfma_bf16_zero_operands", 1)):
         tf, ghz = ctypes.c_double(), ctypes.c_double()
         if lib.fa_probe_mfma_bf16(zero, 20000, ctypes.byref(tf), ctypes.byref(ghz)) != 0:
             return None
         out[name] = {"tflops": tf.value, "shader_clock_ghz": ghz.value}
-    gbs = ctypes.c_double()
-    if lib.fa_probe_hbm_read(4 << 30, 5, ctypes.byref(gbs)) != 0:
-        return None
-    out["hbm_read_gbs"] = gbs.value
+    reads = {}
+    for name, nt in (("plain", 0), ("nontemporal", 1)):
+        gbs = ctypes.c_double()
+        if lib.fa_probe_hbm_read_hint(4 << 30, 5, nt, ctypes.byref(gbs)) != 0:
+            return None
+        reads[name] = gbs.value
+    out["hbm_read_gbs"] = max(reads.values())
+    out["hbm_read_gbs_by_hint"] = reads
     out["note"] = ("whole-chip sustained v_mfma_f32_32x32x16_bf16 rate (two waves per SIMD, operands in "
-                   "registers) and 4 GiB read-only stream with 16-byte loads")
+                   "registers) and a 4 GiB read-only stream with 16-byte loads, with and without the "
+                   "non-temporal hint (hbm_read_gbs is the faster)")
     return out
 
 

@@ -8,8 +8,9 @@
 //     matrix cores draw far less power on zeros, and on a power-limited part
 //     that changes the clock, so the random figure is the relevant ceiling
 //     for attention on random data.
-//   fa_probe_hbm_read: read-only streaming bandwidth over a device buffer
-//     with 16-byte loads, eight in flight per thread.
+//   fa_probe_hbm_read(_hint): read-only streaming bandwidth over a device
+//     buffer with 16-byte loads, eight in flight per thread, with or without
+//     the non-temporal load hint.
 //
 // Both allocate their own buffers and synchronise the device; they are
 // measurement tools, not for use inside a timed region.
@@ -70,6 +71,8 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_peak_kernel(float* out, lon
 constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 8;
 
+// NT: loads carry the non-temporal hint (evict-first), as a one-pass stream would.
+template <bool NT>
 __global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const u32x4* __restrict__ p, size_t n16,
                                                                 uint32_t* out) {
   uint32_t acc = 0;
@@ -78,7 +81,9 @@ __global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const u32x4* __r
     u32x4 v[kReadUnroll];
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u)
-      v[u] = (i + (size_t)u * kReadThreads < n16) ? p[i + (size_t)u * kReadThreads] : u32x4{0u, 0u, 0u, 0u};
+      v[u] = (i + (size_t)u * kReadThreads < n16)
+                 ? (NT ? __builtin_nontemporal_load(&p[i + (size_t)u * kReadThreads]) : p[i + (size_t)u * kReadThreads])
+                 : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -145,8 +150,9 @@ int fa_probe_mfma_bf16(int zero_operands, int iters, double* tflops, double* sha
 }
 
 // Read-only HBM bandwidth (GB/s, decimal) over a buffer of `bytes` bytes
-// (rounded down to 16), averaged over `reps` passes after one warm-up.
-int fa_probe_hbm_read(size_t bytes, int reps, double* gbs) {
+// (rounded down to 16), averaged over `reps` passes after one warm-up; with
+// `nontemporal` the loads carry the non-temporal hint.
+int fa_probe_hbm_read_hint(size_t bytes, int reps, int nontemporal, double* gbs) {
   if (bytes < 16 || reps <= 0 || gbs == nullptr) return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
@@ -165,11 +171,16 @@ int fa_probe_hbm_read(size_t bytes, int reps, double* gbs) {
     if (hipMemset(buf, 1, n16 * 16) != hipSuccess) break;
     if (hipEventCreate(&e.a) != hipSuccess || hipEventCreate(&e.b) != hipSuccess) break;
     const int blocks = 8 * cus;
-    hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(kReadThreads), 0, 0, buf, n16, out);
+    auto launch = [&] {
+      if (nontemporal)
+        hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(blocks), dim3(kReadThreads), 0, 0, buf, n16, out);
+      else
+        hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(blocks), dim3(kReadThreads), 0, 0, buf, n16, out);
+    };
+    launch();
     if (hipDeviceSynchronize() != hipSuccess) break;
     if (hipEventRecord(e.a, 0) != hipSuccess) break;
-    for (int r = 0; r < reps; ++r)
-      hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(kReadThreads), 0, 0, buf, n16, out);
+    for (int r = 0; r < reps; ++r) launch();
     if (hipEventRecord(e.b, 0) != hipSuccess) break;
     if (hipEventSynchronize(e.b) != hipSuccess) break;
     float ms = 0.f;
@@ -181,5 +192,8 @@ int fa_probe_hbm_read(size_t bytes, int reps, double* gbs) {
   (void)hipFree(out);
   return rc;
 }
+
+// The same without the hint.
+int fa_probe_hbm_read(size_t bytes, int reps, double* gbs) { return fa_probe_hbm_read_hint(bytes, reps, 0, gbs); }
 
 }  // extern "C"

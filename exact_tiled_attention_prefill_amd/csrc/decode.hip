@@ -15,7 +15,7 @@
 //     memory requirements for inference in large language models", GQA
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
-//     bf16 path (chunks of 1024, 512 or 256 keys, the largest that keeps
+//     bf16 path (chunks of 2048, 1024, 512 or 256 keys, the largest that keeps
 //       two rounds of resident workgroups busy): the chunk streams through a
 //       ring of 32-key K/V tiles copied HBM -> LDS by global_load_lds_dwordx4
 //       (no VGPR staging).  The ring is only two stages deep so that four
@@ -444,9 +444,11 @@ __device__ __forceinline__ void dec_dma16_addr(const void* addr, uint8_t* lds_wa
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
   asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(m0) : "memory");
 }
-// Most pool pages one chunk touches: 1024 keys over pages of >= 16 keys, plus
-// one page for a chunk that does not start on a page boundary.
-constexpr int kMaxChunkPages = 1024 / 16 + 1;
+// Longest bf16 chunk (keys), and the most pool pages one chunk touches: its
+// keys over pages of >= 16 keys, plus one page for a chunk that does not start
+// on a page boundary.
+constexpr int kMaxChunkB = 2048;
+constexpr int kMaxChunkPages = kMaxChunkB / 16 + 1;
 typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
   typedef __attribute__((address_space(3))) dec_i16x4 lds_t;
@@ -751,13 +753,16 @@ __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) 
 // Query heads per bf16 split workgroup for a GQA group of G heads.
 int bf16_group_tile(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
 
-// Keys per bf16 split workgroup: the largest of 1024, 512, 256 that still
-// gives at least two full rounds of resident workgroups (4 per CU on 256
-// CUs) when every sequence is maxlen long; long chunks amortise the per-chunk
-// prologue and partials, short ones keep small batches parallel.
+// Keys per bf16 split workgroup: the largest of 2048, 1024, 512, 256 that
+// still gives at least two full rounds of resident workgroups (4 per CU on
+// 256 CUs) when every sequence is maxlen long; long chunks amortise the
+// per-chunk prologue and partials, short ones keep small batches parallel.
+// (GQA B64 workload, non-temporal copies: 2048 keys 6.15 TB/s, 1024 6.03,
+// 3072 6.14, 4096 6.02, 512 5.83.)
 int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   const long long rows = (long long)B * Hkv * ((Hq / Hkv) / bf16_group_tile(Hq / Hkv));
-  for (int chunk : {1024, 512}) {
+  static_assert(kMaxChunkB == 2048, "the longest chunk sizes the page-id table");
+  for (int chunk : {2048, 1024, 512}) {
     if (rows * ((maxlen + chunk - 1) / chunk) >= 2048) return chunk;
   }
   return 256;

@@ -91,13 +91,15 @@ def test_paged_ids_outside_pool_are_clamped():
     check_bf16(o, ro, "clamped-id paged decode")
 
 
-def test_paged_decode_workload():
-    """The B64 Hq32 Hkv8 d128 decode workload in 64-key pages: bit-identical to
-    contiguous decode, and against the oracle on sampled sequences."""
+@pytest.mark.parametrize("page", [16, 64])
+def test_paged_decode_workload(page):
+    """The B64 Hq32 Hkv8 d128 decode workload (2048-key chunks) in 16- and
+    64-key pages -- 16-key pages give the most page ids per chunk: bit-identical
+    to contiguous decode, and against the oracle on sampled sequences."""
     cfg = I.DECODE_GQA
     q, kc, vc, ls, scale = I.decode_config_inputs(cfg)
     kcd, vcd = kc.to("cuda"), vc.to("cuda")
-    kp, vp, table, _ = I.paged_cache(kcd, vcd, ls, 64, seed=11)
+    kp, vp, table, _ = I.paged_cache(kcd, vcd, ls, page, seed=11)
     qd, ld, td = q.to("cuda"), ls.to("cuda"), table.to("cuda")
     o = decode_paged(qd, kp, vp, td, ld, scale=scale)
     oc = decode(qd, kcd, vcd, ld, scale=scale)

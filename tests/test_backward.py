@@ -55,7 +55,7 @@ def test_backward_matches_oracle(d, causal, N):
     check_grad(dv, rv, "dv")
 
 
-@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("G", [1, 3, 8])
 @pytest.mark.parametrize("scale", [-0.2, 0.0])
 def test_backward_gqa_and_scale(G, scale):
     q, k, v, do, _ = I.backward_inputs(1, G, 1, 200, 128, seed=G)

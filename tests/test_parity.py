@@ -66,7 +66,7 @@ SMALL = [  # (B, Hkv, G, N, d)
     (1, 1, 1, 1, 128), (1, 1, 1, 2, 64), (2, 1, 2, 63, 128), (1, 2, 1, 64, 64), (1, 1, 4, 65, 128),
     (2, 2, 1, 127, 128), (1, 1, 8, 128, 64), (1, 2, 2, 129, 128), (1, 1, 1, 255, 128),
     (1, 1, 4, 256, 128), (2, 1, 1, 257, 64), (1, 2, 4, 1000, 128), (1, 1, 2, 1000, 64),
-    (1, 1, 1, 513, 128), (1, 2, 8, 777, 128), (1, 1, 2, 4097, 64),
+    (1, 1, 1, 513, 128), (1, 2, 8, 777, 128), (1, 1, 2, 4097, 64), (2, 2, 3, 300, 128), (1, 3, 3, 129, 64),
 ]
 
 

@@ -58,7 +58,7 @@ def test_varlen_mixed_lengths_match_oracle(d, causal, window):
         assert torch.all(o[rows] == 0)
 
 
-@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("G", [1, 3, 8])
 def test_varlen_gqa_groups(G):
     lens = [(300, 300), (100, 513)]
     q, k, v, cu_q, cu_k, scale = I.varlen_inputs(lens, G, 1, 128, seed=G)

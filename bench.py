@@ -337,7 +337,7 @@ def main():
                              workspace=bws)
         vl_legs.append(("backward", bwf, 2.5 * prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True),
                         {"workload": pc.name, "flops": "2.5 x forward (five matrix products per score)",
-                         "kernels": "prep + dQ + dK/dV"}))
+                         "kernels": "dQ (with the D and lse rows) + dK/dV"}))
 
     for _ in range(args.warmup):
         for _, vf, _, _ in vl_legs:
@@ -440,7 +440,7 @@ def main():
         tf = flops / (avg * 1e-3) / 1e12
         result[name] = {"config": cfg, "ms_avg": avg, "ms_median": ms[K // 2], "ms_min": ms[0], "tflops": tf,
                         "flops_per_launch": flops,
-                        "roofline": {"kernel": ("bwd_prep + bwd_dq + bwd_dkdv" if name == "backward"
+                        "roofline": {"kernel": ("bwd_dq + bwd_dkdv" if name == "backward"
                                                 else "prefill_bf16_kernel<128,causal,varlen>"), "bound": "mfma",
                                      "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                      "frac": tf / PEAK_BF16_TFLOPS}}

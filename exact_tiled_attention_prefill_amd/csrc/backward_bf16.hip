@@ -9,20 +9,21 @@
 // (D_i is the row sum of P o dP).  Under GQA a key/value head's dK, dV sum
 // over the query heads that share it.
 //
-// Three kernels on the caller's stream:
-//   prep:  D_i and lse_i*log2(e) per query row into a workspace padded to
-//          64-row multiples (so tile copies never leave it);
-//   dQ:    one workgroup per 128 query rows (as the forward): key tiles
-//          stream through an LDS ring; per 64-key tile and wave
-//          S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T,
-//          with dS^T packed to bf16 straight from the accumulator layout
-//          into the B operand (48 MFMAs);
-//   dK/dV: one workgroup per 128 keys of one key/value head, looping over
-//          the group's query heads and their 64-row query tiles: per wave of
-//          32 keys S = Q K^T and dP = dO V^T (K, V fragments in registers),
-//          then dV += P^T dO and dK += dS^T Q with the packed P / dS as the A
-//          operand (64 MFMAs).  No atomics: every output element has one
-//          writer, so results are deterministic.
+// Two kernels on the caller's stream:
+//   dQ:    one workgroup per 128 query rows (as the forward).  It first
+//          computes D_i and lse_i*log2(e) of its rows and writes them to a
+//          workspace padded to 64-row multiples (so the dK/dV kernel's tile
+//          copies never leave it).  Key tiles then stream through an LDS ring;
+//          per 64-key tile and wave S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
+//          then dQ^T += K^T dS^T, with dS^T packed to bf16 straight from the
+//          accumulator layout into the B operand (48 MFMAs);
+//   dK/dV: one workgroup of 8 waves per 128 keys of one key/value head,
+//          looping over the group's query heads and their 64-row query
+//          tiles.  Waves w and w+4 own the same 32 keys and split each tile's
+//          rows; per wave S = Q K^T and dP = dO V^T (K fragments in registers,
+//          the block's V rows in LDS), then dV += P^T dO and dK += dS^T Q with
+//          the packed P / dS as the A operand (32 MFMAs).  No atomics: every
+//          output element has one writer, so results are deterministic.
 // Q, dO (dK/dV kernel) and K (dQ kernel) are read from LDS both row-wise
 // (ds_read_b128) and transposed (ds_read_b64_tr_b16); their 16-byte chunks
 // use one XOR swizzle that leaves both access patterns free of bank
@@ -81,48 +82,16 @@ __device__ __forceinline__ u32x2 bread_tr(const uint8_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: D_i = dO_i . O_i and lse_i * log2(e); rows >= N of the padded
-// workspace get 0.  D/8 lanes per row, one 16-byte chunk each.
-template <int D>
-__global__ __launch_bounds__(kBThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
-                                                             const uint16_t* __restrict__ dout,
-                                                             const float* __restrict__ lse,
-                                                             float* __restrict__ lse2w, float* __restrict__ dw,
-                                                             int N, int Npad, long long rows) {
-  constexpr int LPR = D / 8;
-  const long long gid = (long long)blockIdx.x * kBThreads + threadIdx.x;
-  const long long prow = gid / LPR;  // padded row index over [B*H*Npad]
-  const int j = (int)(gid % LPR);
-  float acc = 0.f;
-  const long long bh = prow / Npad;
-  const int i = (int)(prow - bh * Npad);
-  const bool valid = prow < rows && i < N;
-  if (valid) {
-    const size_t off = ((size_t)bh * N + i) * D + j * 8;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + off);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + off);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc = fmaf(bf16lo_to_f32(a[t]), bf16lo_to_f32(b[t]), acc);
-      acc = fmaf(bf16hi_to_f32(a[t]), bf16hi_to_f32(b[t]), acc);
-    }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (j == 0 && prow < rows) {
-    dw[prow] = valid ? acc : 0.f;
-    lse2w[prow] = valid ? lse[(size_t)bh * N + i] * kLog2e : 0.f;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dQ kernel.
+// Before its key loop it also computes, for its own rows, D_i = dO_i . O_i and
+// lse_i * log2(e), and writes them to the workspace for the dK/dV kernel
+// (rows N .. Npad-1 of the padded workspace get 0).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2w, const float* __restrict__ dw,
-    uint16_t* __restrict__ dq, int Hq, int Hkv, int N, int Npad, int n_qtiles, int n_items, float cs,
-    float scale) {
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ lse2w, float* __restrict__ dw, uint16_t* __restrict__ dq, int Hq, int Hkv, int N,
+    int Npad, int n_qtiles, int n_items, float cs, float scale) {
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int RC = D / 8;
@@ -178,8 +147,31 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
       df[t] = __builtin_bit_cast(bf16x8, wd[t] & keep);
     }
   }
-  const float l2 = lse2w[(size_t)bh * Npad + qr];
-  const float dd = dw[(size_t)bh * Npad + qr];
+  // D and lse*log2(e) of row qrow: each half-wave lane holds half of the
+  // row's d elements (the same split as df), the other half is in lane x^32
+  float dd, l2;
+  {
+    const uint16_t* op = o + qbase + (size_t)qr * D + hi * 8;
+    u32x4 wo[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) wo[t] = *reinterpret_cast<const u32x4*>(op + t * 16);
+    float a = 0.f;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const u32x4 dv4 = __builtin_bit_cast(u32x4, df[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a = fmaf(bf16lo_to_f32(wo[t][e]), bf16lo_to_f32(dv4[e]), a);
+        a = fmaf(bf16hi_to_f32(wo[t][e]), bf16hi_to_f32(dv4[e]), a);
+      }
+    }
+    dd = sum_halves(a);
+    l2 = qrow < N ? lse[(size_t)bh * N + qr] * kLog2e : 0.f;
+    if (hi == 0 && qrow < Npad) {
+      dw[(size_t)bh * Npad + qrow] = dd;  // 0 past N: dO was zeroed there
+      lse2w[(size_t)bh * Npad + qrow] = l2;
+    }
+  }
 
   // LDS read offsets.  K rows (both patterns): row x (+32mb), chunk (2ks+hi)^swz_both
   int koff[KS], voff_r[KS];
@@ -529,16 +521,6 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   const int Npad = (a.N + kBTile - 1) / kBTile * kBTile;
   float* lse2w = static_cast<float*>(a.ws);
   float* dw = lse2w + (size_t)a.B * a.Hq * Npad;
-  const long long rows = (long long)a.B * a.Hq * Npad;
-  const long long prep_threads = rows * (D / 8);
-  const long long prep_blocks = (prep_threads + kBThreads - 1) / kBThreads;
-  if (prep_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_blocks), dim3(kBThreads), 0, stream,
-                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, lse2w, dw,
-                     a.N, Npad, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
   const float cs = a.scale * kLog2e;  // signed: exp2(s_raw * cs - lse * log2 e)
   const int n_qtiles = (a.N + kBQRows - 1) / kBQRows;
   const long long dq_items = (long long)n_qtiles * a.B * a.Hq;
@@ -547,9 +529,10 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   if (dq_items > 0x7fffffffLL || kv_items > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)dq_items), dim3(kBThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), lse2w, dw,
-                     static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, Npad, n_qtiles, (int)dq_items, cs, a.scale);
-  e = hipGetLastError();
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.o),
+                     static_cast<const uint16_t*>(a.dout), a.lse, lse2w, dw, static_cast<uint16_t*>(a.dq), a.Hq,
+                     a.Hkv, a.N, Npad, n_qtiles, (int)dq_items, cs, a.scale);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)kv_items), dim3(kBKThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),

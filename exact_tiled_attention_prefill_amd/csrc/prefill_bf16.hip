@@ -64,10 +64,12 @@
 namespace fa {
 namespace {
 
-// Launch shape (compile-time): waves per workgroup and keys per tile.  Eight
-// waves (256 query rows sharing each K/V tile) halve the L2 -> LDS traffic and
-// run 3-5% faster from 8K keys on, but lose at 1K-4K, where one workgroup per
-// CU leaves its prologue and the wider causal diagonal exposed.
+// Launch shape (compile-time): waves per workgroup and keys per tile.  Both
+// alternatives pass the same parity tests.  Eight waves (256 query rows
+// sharing each K/V tile) halve the L2 -> LDS traffic and gain 1-2% from 8K
+// keys on, but lose at 1K-4K causal, where one workgroup per CU leaves its
+// prologue and the wider causal diagonal exposed; 32-key tiles are ~3%
+// slower.
 #ifndef FA_PREFILL_WAVES
 #define FA_PREFILL_WAVES 4
 #endif
@@ -77,7 +79,7 @@ namespace {
 constexpr int kWaves = FA_PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;       // query rows per workgroup
-constexpr int kBC = FA_PREFILL_BC;     // keys per tile (32 or 64)
+constexpr int kBC = FA_PREFILL_BC;     // keys per tile (64, or 32)
 constexpr int kMB = kBC / 32;          // 32-key MFMA blocks per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 

@@ -220,9 +220,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 16K and 128K causal GQA prefill configurations")
     ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "prefill_chunked", "prefill_window",
-                                       "backward", "copy", "ceiling"], default=None,
+                                       "backward", "prefill_gqa_16k", "prefill_gqa_128k", "copy", "ceiling"],
+                    default=None,
                     help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
                          "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
                          "MFMA / HBM ceiling probes")
@@ -458,12 +461,48 @@ def main():
                                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
+    # the other two causal GQA configurations, timed after the steps above
+    # with their own (smaller) step counts: B2 Hq32 Hkv8 N16384 and
+    # B1 Hq64 Hkv8 N131072 (O(N) memory: no N x N buffer exists anywhere)
+    cfg_legs = []
+    for name, cfg, steps in (("prefill_gqa_16k", I.PREFILL_GQA_16K, max(1, min(K, 10))),
+                             ("prefill_gqa_128k", I.PREFILL_GQA_128K, max(1, min(K, 3)))):
+        if not (args.only == name or (args.only is None and not args.no_configs)):
+            continue
+        cq, ck_, cv, cscale = I.prefill_config_inputs(cfg)
+        cqd, ckd_, cvd = cq.to(dev), ck_.to(dev), cv.to(dev)
+        del cq, ck_, cv
+        cod = torch.empty_like(cqd)
+        cld = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
+        prefill(cqd, ckd_, cvd, causal=True, scale=cscale, out=cod, lse=cld)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            prefill(cqd, ckd_, cvd, causal=True, scale=cscale, out=cod, lse=cld)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        avg = sum(ms) / steps
+        F = prefill_flops(cfg.B, cfg.Hq, cfg.N, cfg.d, True)
+        tf = F / (avg * 1e-3) / 1e12
+        result[name] = {"workload": cfg.name, "steps": steps, "ms_avg": avg, "ms_median": ms[steps // 2],
+                        "ms_min": ms[0], "tflops": tf, "tokens_per_s": cfg.B * cfg.N / (avg * 1e-3),
+                        "flops_per_launch": F,
+                        "roofline": {"kernel": "prefill_bf16_kernel<128,causal>", "bound": "mfma", "achieved": tf,
+                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}
+        cfg_legs.append(name)
+        del cqd, ckd_, cvd, cod, cld
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"] = tf
     if args.only is None and not args.no_ceilings:
         ceil = measured_ceilings()
         result["ceilings"] = ceil
         if ceil is not None:
             sus = ceil["mfma_bf16_random_operands"]["tflops"]
-            for rl in [result.get("roofline")] + [result[n]["roofline"] for n, _, _, _ in vl_legs]:
+            for rl in ([result.get("roofline")] + [result[n]["roofline"] for n, _, _, _ in vl_legs]
+                       + [result[n]["roofline"] for n in cfg_legs]):
                 if rl is not None:
                     rl["measured_ceiling"] = sus
                     rl["frac_of_measured_ceiling"] = rl["achieved"] / sus

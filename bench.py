@@ -18,7 +18,7 @@ fp64 CPU oracle is timed on the host as a reported baseline, and the
 device's sustained MFMA and HBM-read rates are measured after the timed
 region.
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: the kernels run on one GPU.
 """
 
 import argparse

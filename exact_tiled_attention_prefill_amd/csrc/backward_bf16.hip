@@ -30,6 +30,7 @@
 // conflicts.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -173,13 +174,12 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     }
   }
 
-  // LDS read offsets.  K rows (both patterns): row x (+32mb), chunk (2ks+hi)^swz_both
-  int koff[KS], voff_r[KS];
+  // LDS read offsets.  K and V rows: row x (+32mb), chunk (2ks+hi)^swz_both.
+  // V is only read row-wise, but sharing K's swizzle (a permutation over any
+  // 16 rows, so row reads stay conflict-free) lets both use one offset set.
+  int koff[KS];
 #pragma unroll
-  for (int t = 0; t < KS; ++t) {
-    koff[t] = x * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
-    voff_r[t] = x * (D * 2) + (((2 * t + hi) ^ swz_row<D>(x)) << 4);
-  }
+  for (int t = 0; t < KS; ++t) koff[t] = x * (D * 2) + (((2 * t + hi) ^ swz_both<D>(x)) << 4);
   // K^T transposed reads: rows 4hi + (i>>2) (+8 for the second half, +16ks2),
   // column block md; the swizzle depends on row bits 0..3, so the +8 half
   // has its own offset (+16 rows leave it unchanged)
@@ -195,27 +195,33 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
         ktr[md][hf] = row * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
     }
   }
-  // DMA offsets: chunk p = i*256 + tid -> row p / RC, chunk p % RC
+  // DMA: chunk p = i*256 + tid -> row p / RC, chunk p % RC.  A lane's chunks
+  // are kRowStep rows apart and both swizzles depend on the row only modulo
+  // 16, so one offset serves every chunk; the row step goes into the base.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t dk_off[CPT], dv_off[CPT];
-  int drow[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int p = i * kBThreads + wave * 64 + lane;
-    const int r = p / RC, cp = p % RC;
-    drow[i] = r;
-    dk_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_both<D>(r)) << 4));
-    dv_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_row<D>(r)) << 4));
-  }
-  auto issue = [&](int t, int st) {
+  constexpr int kRowStep = kBThreads / RC;
+  static_assert(kRowStep % 16 == 0, "row step keeps the swizzle");
+  const int drow = (wave * 64 + lane) / RC, dcp = lane % RC;
+  const uint32_t d_off = (uint32_t)(drow * D * 2 + ((dcp ^ swz_both<D>(drow)) << 4));
+  auto issue = [&](int t, uint8_t* kdst, uint8_t* vdst) {
     const int k0 = t * kBTile;
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(kh) + (size_t)k0 * D * 2;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(vh) + (size_t)k0 * D * 2;
+    if (k0 + kBTile <= N) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int delta = (k0 + kBTile <= N) ? 0 : (min(drow[i], N - 1 - k0) - drow[i]) * D * 2;
-      bdma16(kb, dk_off[i] + delta, ring[st][0] + (i * kBThreads + wave_s * 64) * 16);
-      bdma16(vb, dv_off[i] + delta, ring[st][1] + (i * kBThreads + wave_s * 64) * 16);
+      for (int i = 0; i < CPT; ++i) {
+        bdma16(kb + (size_t)i * kRowStep * D * 2, d_off, kdst + (i * kBThreads + wave_s * 64) * 16);
+        bdma16(vb + (size_t)i * kRowStep * D * 2, d_off, vdst + (i * kBThreads + wave_s * 64) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        // rows past the end re-read the last row; the offset is taken from
+        // the tile base and the clamped row is >= 0, so it never wraps
+        const int delta = (min(drow + i * kRowStep, N - 1 - k0) - drow) * D * 2;
+        bdma16(kb, d_off + delta, kdst + (i * kBThreads + wave_s * 64) * 16);
+        bdma16(vb, d_off + delta, vdst + (i * kBThreads + wave_s * 64) * 16);
+      }
     }
   };
 
@@ -225,13 +231,20 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBQRows) : N;
   const int ntiles = (kv_end + kBTile - 1) / kBTile;
-  issue(0, 0);
-  bwait_vmem_le<0>();
-  bbarrier();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    const uint8_t* kl = ring[t & 1][0];
-    const uint8_t* vl = ring[t & 1][1];
+  // Every row of this wave sees every key of tile k0 (no per-element mask):
+  // the tile lies below the causal diagonal of the wave's first row and
+  // inside the sequence.  Wave-uniform.
+  const int wave_first_s = q0 + wave_s;
+  auto tile_all_visible = [&](int k0) {
+    return k0 + kBTile <= N && (!CAUSAL || k0 + kBTile - 1 <= wave_first_s);
+  };
+  // One tile step; the ring slot is a compile-time constant (the loop is
+  // unrolled by two), so the LDS reads take immediate offsets.
+  auto step = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (t + 1 < ntiles) issue(t + 1, ring[SL ^ 1][0], ring[SL ^ 1][1]);
+    const uint8_t* kl = ring[SL][0];
+    const uint8_t* vl = ring[SL][1];
     const int k0 = t * kBTile;
     if (wave_has_rows && (!CAUSAL || k0 <= wave_last_row)) {
       f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -246,19 +259,26 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
       for (int t2 = 0; t2 < KS; ++t2)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + voff_r[t2] + mb * 32 * D * 2);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + koff[t2] + mb * 32 * D * 2);
           dp[mb] = mfma32x32x16(vf, df[t2], dp[mb]);
         }
-      // key of (mb, r) = k0 + 4hi + 32mb + 8(r/4) + r%4; visible when <= lim
-      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool vis = 32 * mb + 8 * (r >> 2) + (r & 3) <= lim;
-          const float p = vis ? fast_exp2(fmaf(s[mb][r], cs, -l2)) : 0.f;
-          s[mb][r] = p * (dp[mb][r] - dd);  // dS^T
-        }
+        for (int r = 0; r < 16; ++r) s[mb][r] = fast_exp2(fmaf(s[mb][r], cs, -l2));  // P^T
+      if (!tile_all_visible(k0)) {
+        // key of (mb, r) = k0 + 4hi + 32mb + 8(r/4) + r%4; visible when <= lim
+        // (a select, not a product: a masked exponent may be +inf)
+        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[mb][r] = 32 * mb + 8 * (r >> 2) + (r & 3) <= lim ? s[mb][r] : 0.f;
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][r] *= dp[mb][r] - dd;  // dS^T
 #pragma unroll
       for (int ks2 = 0; ks2 < kBTile / 16; ++ks2) {
         float tmp[8];
@@ -276,7 +296,16 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     }
     if (t + 1 < ntiles) bwait_vmem_le<0>();
     bbarrier();
+  };
+  issue(0, ring[0][0], ring[0][1]);
+  bwait_vmem_le<0>();
+  bbarrier();
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
   if (wave_has_rows && qrow < N) {
     uint16_t* orow = dq + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -379,15 +408,12 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
         trr[md][hf] = (32 * half + row) * (D * 2) + (((4 * md + colc) ^ swz_both<D>(row)) << 4) + 8 * (i & 1);
     }
   }
-  uint32_t d_off[CPT];
-  int drow[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int p = i * kBKThreads + wave * 64 + lane;
-    const int r = p / RC, cp = p % RC;
-    drow[i] = r;
-    d_off[i] = (uint32_t)(r * D * 2 + ((cp ^ swz_both<D>(r)) << 4));
-  }
+  // one DMA offset per lane: its chunks are kRowStep rows apart and the
+  // swizzle depends on the row only modulo 16
+  constexpr int kRowStep = kBKThreads / RC;
+  static_assert(kRowStep % 16 == 0, "row step keeps the swizzle");
+  const int drow = (wave * 64 + lane) / RC;
+  const uint32_t d_off = (uint32_t)(drow * D * 2 + (((lane % RC) ^ swz_both<D>(drow)) << 4));
 
   f32x16 dva[MD], dka[MD];
 #pragma unroll
@@ -401,17 +427,27 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
   const int per_head = n_qt - qt0;
   const int total = per_head * G;               // (head, query tile) steps
   // step u: head h = g*G + u / per_head, query tile qt0 + u % per_head
-  auto issue = [&](int u, int st) {
+  auto issue = [&](int u, auto st_c) {
+    constexpr int st = decltype(st_c)::value;
     const int h = g * G + u / per_head;
     const int q0 = (qt0 + u % per_head) * kBTile;
     const size_t hb = ((size_t)b * Hq + h);
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(q + hb * N * D) + (size_t)q0 * D * 2;
     const uint8_t* ob = reinterpret_cast<const uint8_t*>(dout + hb * N * D) + (size_t)q0 * D * 2;
+    if (q0 + kBTile <= N) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int delta = (q0 + kBTile <= N) ? 0 : (min(drow[i], N - 1 - q0) - drow[i]) * D * 2;
-      bdma16(qb, d_off[i] + delta, ring[st][0] + (i * kBKThreads + wave_s * 64) * 16);
-      bdma16(ob, d_off[i] + delta, ring[st][1] + (i * kBKThreads + wave_s * 64) * 16);
+      for (int i = 0; i < CPT; ++i) {
+        bdma16(qb + (size_t)i * kRowStep * D * 2, d_off, ring[st][0] + (i * kBKThreads + wave_s * 64) * 16);
+        bdma16(ob + (size_t)i * kRowStep * D * 2, d_off, ring[st][1] + (i * kBKThreads + wave_s * 64) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        // clamped row >= 0 relative to the tile base: the offset never wraps
+        const int delta = (min(drow + i * kRowStep, N - 1 - q0) - drow) * D * 2;
+        bdma16(qb, d_off + delta, ring[st][0] + (i * kBKThreads + wave_s * 64) * 16);
+        bdma16(ob, d_off + delta, ring[st][1] + (i * kBKThreads + wave_s * 64) * 16);
+      }
     }
     // lse2 / D of the tile's 64 rows (padded workspace, always in range):
     // waves 0-1 copy lse2, waves 2-3 copy D, 8 lanes x 16 bytes each
@@ -422,15 +458,23 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  if (total > 0) issue(0, 0);
-  bwait_vmem_le<0>();  // the V block (and tile 0)
-  bbarrier();
-  for (int u = 0; u < total; ++u) {
-    if (u + 1 < total) issue(u + 1, (u + 1) & 1);
-    const uint8_t* ql = ring[u & 1][0];
-    const uint8_t* ol = ring[u & 1][1];
-    const float* l2t = rowv[u & 1][0];
-    const float* ddt = rowv[u & 1][1];
+  // Every (row, key) pair of this wave in the tile at q0 is visible (no
+  // per-element mask): the wave's rows lie inside the sequence and, causal,
+  // at or below the diagonal of its last key.  Wave-uniform.
+  const int wkey_last = k0b + 32 * (wave_s & 3) + 31;
+  const int wrow_off = 32 * (wave_s >> 2);
+  auto tile_all_visible = [&](int q0) {
+    return q0 + wrow_off + 31 < N && (!CAUSAL || wkey_last <= q0 + wrow_off);
+  };
+  // One (head, query tile) step; the ring slot is a compile-time constant
+  // (the loop is unrolled by two), so the LDS reads take immediate offsets.
+  auto step = [&](int u, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (u + 1 < total) issue(u + 1, std::integral_constant<int, SL ^ 1>{});
+    const uint8_t* ql = ring[SL][0];
+    const uint8_t* ol = ring[SL][1];
+    const float* l2t = rowv[SL][0];
+    const float* ddt = rowv[SL][1];
     const int q0 = (qt0 + u % per_head) * kBTile;
     // S[q, key] = Q K^T and dP[q, key] = dO V^T over rows q0 + 32half + 8(r/4) + 4hi + r%4
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -446,19 +490,24 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
       dp = mfma32x32x16(a, bv, dp);
     }
     // P and dS (visible: row < N and, causal, key <= row)
+    const bool all_vis = tile_all_visible(q0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = 32 * half + 8 * j + 4 * hi;  // first of the 4 rows
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2t + rr);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(ddt + rr);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = q0 + rr + e;
-        const bool vis = row < N && (!CAUSAL || key <= row);
-        const float p = vis ? fast_exp2(fmaf(s[4 * j + e], cs, -l4[e])) : 0.f;
-        s[4 * j + e] = p;                           // P
-        dp[4 * j + e] = p * (dp[4 * j + e] - d4[e]);  // dS
+      for (int e = 0; e < 4; ++e) s[4 * j + e] = fast_exp2(fmaf(s[4 * j + e], cs, -l4[e]));
+      if (!all_vis) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = q0 + rr + e;
+          const bool vis = row < N && (!CAUSAL || key <= row);
+          s[4 * j + e] = vis ? s[4 * j + e] : 0.f;
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * j + e] = s[4 * j + e] * (dp[4 * j + e] - d4[e]);  // dS
     }
     // dV += P^T dO and dK += dS^T Q over two 16-row steps of the wave's rows
 #pragma unroll
@@ -485,7 +534,16 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
     }
     if (u + 1 < total) bwait_vmem_le<0>();
     bbarrier();
+  };
+  if (total > 0) issue(0, std::integral_constant<int, 0>{});
+  bwait_vmem_le<0>();  // the V block (and tile 0)
+  bbarrier();
+  int u = 0;
+  for (; u + 1 < total; u += 2) {
+    step(u, std::integral_constant<int, 0>{});
+    step(u + 1, std::integral_constant<int, 1>{});
   }
+  if (u < total) step(u, std::integral_constant<int, 0>{});
 
   // Sum the two halves through LDS (every wave is past the last barrier, no
   // copy is in flight), then the lower waves store.  Register r of block md

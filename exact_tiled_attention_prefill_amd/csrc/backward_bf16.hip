@@ -11,7 +11,7 @@
 //
 // Two kernels on the caller's stream:
 //   dQ:    one workgroup per 128 query rows (as the forward).  It first
-//          computes D_i and lse_i*log2(e) of its rows and writes them to a
+//          computes D_i of its rows and writes -D_i and -lse_i*log2(e) to a
 //          workspace padded to 64-row multiples (so the dK/dV kernel's tile
 //          copies never leave it).  Key tiles then stream through an LDS ring;
 //          per 64-key tile and wave S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
@@ -22,8 +22,11 @@
 //          tiles.  Waves w and w+4 own the same 32 keys and split each tile's
 //          rows; per wave S = Q K^T and dP = dO V^T (K fragments in registers,
 //          the block's V rows in LDS), then dV += P^T dO and dK += dS^T Q with
-//          the packed P / dS as the A operand (32 MFMAs).  No atomics: every
-//          output element has one writer, so results are deterministic.
+//          the packed P / dS as the A operand (32 MFMAs).  The dP
+//          accumulator starts at -D of its rows, so dS = P dP takes one
+//          product, and the exponentials (and dS) run under the dP (and dV)
+//          matrix products.  No atomics: every output element has
+//          one writer, so results are deterministic.
 // Q, dO (dK/dV kernel) and K (dQ kernel) are read from LDS both row-wise
 // (ds_read_b128) and transposed (ds_read_b64_tr_b16); their 16-byte chunks
 // use one XOR swizzle that leaves both access patterns free of bank
@@ -84,14 +87,14 @@ __device__ __forceinline__ u32x2 bread_tr(const uint8_t* p) {
 
 // ---------------------------------------------------------------------------
 // dQ kernel.
-// Before its key loop it also computes, for its own rows, D_i = dO_i . O_i and
-// lse_i * log2(e), and writes them to the workspace for the dK/dV kernel
+// Before its key loop it also computes, for its own rows, D_i = dO_i . O_i,
+// and writes -D_i and -lse_i * log2(e) to the workspace for the dK/dV kernel
 // (rows N .. Npad-1 of the padded workspace get 0).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ lse2w, float* __restrict__ dw, uint16_t* __restrict__ dq, int Hq, int Hkv, int N,
+    float* __restrict__ nlsw, float* __restrict__ ndw, uint16_t* __restrict__ dq, int Hq, int Hkv, int N,
     int Npad, int n_qtiles, int n_items, float cs, float scale) {
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     dd = sum_halves(a);
     l2 = qrow < N ? lse[(size_t)bh * N + qr] * kLog2e : 0.f;
     if (hi == 0 && qrow < Npad) {
-      dw[(size_t)bh * Npad + qrow] = dd;  // 0 past N: dO was zeroed there
-      lse2w[(size_t)bh * Npad + qrow] = l2;
+      ndw[(size_t)bh * Npad + qrow] = -dd;  // 0 past N: dO was zeroed there
+      nlsw[(size_t)bh * Npad + qrow] = -l2;
     }
   }
 
@@ -331,7 +334,7 @@ constexpr int kBKThreads = 512;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2w, const float* __restrict__ dw,
+    const uint16_t* __restrict__ dout, const float* __restrict__ nlsw, const float* __restrict__ ndw,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, int Npad, int n_kblocks,
     int n_items, float cs, float scale) {
   constexpr int KS = D / 16;
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
   // [stage][Q, dO] tiles; at the end the ring holds the upper waves' partial sums
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vblk[kBKeys * D * 2];
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBTile];  // [stage][lse2, D][row]
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][kBTile];  // [stage][-lse*log2(e), -D][row]
   static_assert(4 * 32 * D * 4 <= 2 * 2 * TILE, "partial sums must fit in the ring");
 
   const int tid = threadIdx.x;
@@ -449,12 +452,16 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
         bdma16(ob, d_off + delta, ring[st][1] + (i * kBKThreads + wave_s * 64) * 16);
       }
     }
-    // lse2 / D of the tile's 64 rows (padded workspace, always in range):
-    // waves 0-1 copy lse2, waves 2-3 copy D, 8 lanes x 16 bytes each
+    // -lse*log2(e) and -D of the tile's 64 rows (padded workspace, always in
+    // range): waves 0-1 copy the first, waves 2-3 the second, 8 lanes x 16
+    // bytes each
     if (wave_s < 4) {
-      const void* src = sgpr_ptr((wave_s < 2 ? lse2w : dw) + hb * Npad + q0 + 32 * (wave_s & 1));
-      if (lane < 8)
-        bdma16(src, (uint32_t)(lane * 16), reinterpret_cast<uint8_t*>(&rowv[st][wave_s >> 1][32 * (wave_s & 1)]));
+      const void* src = sgpr_ptr((wave_s < 2 ? nlsw : ndw) + hb * Npad + q0 + 32 * (wave_s & 1));
+      // the lane id is taken afresh (mbcnt): a value kept live across the
+      // loop was spilled, and its reload's vmcnt wait stalled on the copies
+      const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      if (ln < 8)
+        bdma16(src, ln * 16, reinterpret_cast<uint8_t*>(&rowv[st][wave_s >> 1][32 * (wave_s & 1)]));
     }
   };
 
@@ -473,70 +480,113 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
     if (u + 1 < total) issue(u + 1, std::integral_constant<int, SL ^ 1>{});
     const uint8_t* ql = ring[SL][0];
     const uint8_t* ol = ring[SL][1];
-    const float* l2t = rowv[SL][0];
-    const float* ddt = rowv[SL][1];
+    const float* nlt = rowv[SL][0];
+    const float* ndt = rowv[SL][1];
     const int q0 = (qt0 + u % per_head) * kBTile;
-    // S[q, key] = Q K^T and dP[q, key] = dO V^T over rows q0 + 32half + 8(r/4) + 4hi + r%4
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // S[q, key] = Q K^T and dP[q, key] = dO V^T - D over rows
+    // q0 + 32half + 8(r/4) + 4hi + r%4: the dP accumulator starts at the
+    // rows' -D, so dS = P dP.
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ndt + 32 * half + 8 * j + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * j + e] = d4[e];
+    }
+    // The regions below are fenced (sched_barrier) so that each one's
+    // grouping hints see only its own instructions.
+    // region 1: S (and the rows' -lse log2 e)
 #pragma unroll
     for (int t2 = 0; t2 < KS; ++t2) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + roff[t2]);
       s = mfma32x32x16(a, kf[t2], s);
     }
+    f32x4 l4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l4[j] = *reinterpret_cast<const f32x4*>(nlt + 32 * half + 8 * j + 4 * hi);
+    __builtin_amdgcn_sched_barrier(0);
+    // region 2: dP || P = exp2(cs S - lse log2 e)
 #pragma unroll
     for (int t2 = 0; t2 < KS; ++t2) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + roff[t2]);
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vblk + voffb[t2]);
       dp = mfma32x32x16(a, bv, dp);
     }
-    // P and dS (visible: row < N and, causal, key <= row)
-    const bool all_vis = tile_all_visible(q0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 32 * half + 8 * j + 4 * hi;  // first of the 4 rows
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2t + rr);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ddt + rr);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * j + e] = fast_exp2(fmaf(s[4 * j + e], cs, -l4[e]));
-      if (!all_vis) {
+      for (int e = 0; e < 4; ++e) s[4 * j + e] = fast_exp2(fmaf(s[4 * j + e], cs, l4[j][e]));
+    // one matrix product and four VALU ops per step
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = q0 + rr + e;
-          const bool vis = row < N && (!CAUSAL || key <= row);
-          s[4 * j + e] = vis ? s[4 * j + e] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dp[4 * j + e] = s[4 * j + e] * (dp[4 * j + e] - d4[e]);  // dS
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    // dV += P^T dO and dK += dS^T Q over two 16-row steps of the wave's rows
+    __builtin_amdgcn_sched_barrier(0);
+    // visible: row < N and, causal, key <= row (a select: a masked exponent
+    // may be +inf)
+    if (!tile_all_visible(q0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = q0 + 32 * half + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool vis = row < N && (!CAUSAL || key <= row);
+        s[r] = vis ? s[r] : 0.f;
+      }
+    }
+    // region 3: dV += P^T dO || dS = P dP
+    bf16x8 pa[2], da[2];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      float tp[8], td[8];
+      float tp[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tp[j] = s[8 * ks2 + j];
-        td[j] = dp[8 * ks2 + j];
-      }
-      const bf16x8 pa = pack_bf16x8(tp);
-      const bf16x8 da = pack_bf16x8(td);
+      for (int j = 0; j < 8; ++j) tp[j] = s[8 * ks2 + j];
+      pa[ks2] = pack_bf16x8(tp);
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
         const u32x2 o0 = bread_tr(ol + trr[md][0] + (16 * ks2) * D * 2);
         const u32x2 o1 = bread_tr(ol + trr[md][1] + (16 * ks2) * D * 2);
         const u32x4 ob = {o0[0], o0[1], o1[0], o1[1]};
-        dva[md] = mfma32x32x16(pa, __builtin_bit_cast(bf16x8, ob), dva[md]);
+        dva[md] = mfma32x32x16(pa[ks2], __builtin_bit_cast(bf16x8, ob), dva[md]);
+      }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      float td[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) td[j] = s[8 * ks2 + j] * dp[8 * ks2 + j];
+      da[ks2] = pack_bf16x8(td);
+    }
+    // the first probabilities' packs, then one matrix product and three VALU
+    // ops per step
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * MD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // region 4: dK += dS^T Q
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
         const u32x2 q0r = bread_tr(ql + trr[md][0] + (16 * ks2) * D * 2);
         const u32x2 q1r = bread_tr(ql + trr[md][1] + (16 * ks2) * D * 2);
         const u32x4 qbv = {q0r[0], q0r[1], q1r[0], q1r[1]};
-        dka[md] = mfma32x32x16(da, __builtin_bit_cast(bf16x8, qbv), dka[md]);
+        dka[md] = mfma32x32x16(da[ks2], __builtin_bit_cast(bf16x8, qbv), dka[md]);
       }
-    }
     if (u + 1 < total) bwait_vmem_le<0>();
     bbarrier();
   };
   if (total > 0) issue(0, std::integral_constant<int, 0>{});
   bwait_vmem_le<0>();  // the V block (and tile 0)
+  // The K fragments' loads have landed too.  A use of them here lets the
+  // compiler settle their wait before the loop; otherwise it waits inside
+  // the loop, where its vmcnt also counts the next tile's copies.
+#pragma unroll
+  for (int t = 0; t < KS; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, kf[t])));
   bbarrier();
   int u = 0;
   for (; u + 1 < total; u += 2) {
@@ -577,8 +627,8 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   const int Npad = (a.N + kBTile - 1) / kBTile * kBTile;
-  float* lse2w = static_cast<float*>(a.ws);
-  float* dw = lse2w + (size_t)a.B * a.Hq * Npad;
+  float* nlsw = static_cast<float*>(a.ws);  // -lse/scale, then -D, per padded row
+  float* ndw = nlsw + (size_t)a.B * a.Hq * Npad;
   const float cs = a.scale * kLog2e;  // signed: exp2(s_raw * cs - lse * log2 e)
   const int n_qtiles = (a.N + kBQRows - 1) / kBQRows;
   const long long dq_items = (long long)n_qtiles * a.B * a.Hq;
@@ -588,13 +638,13 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)dq_items), dim3(kBThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.o),
-                     static_cast<const uint16_t*>(a.dout), a.lse, lse2w, dw, static_cast<uint16_t*>(a.dq), a.Hq,
+                     static_cast<const uint16_t*>(a.dout), a.lse, nlsw, ndw, static_cast<uint16_t*>(a.dq), a.Hq,
                      a.Hkv, a.N, Npad, n_qtiles, (int)dq_items, cs, a.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)kv_items), dim3(kBKThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), lse2w, dw,
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), nlsw, ndw,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, Npad, n_kblocks,
                      (int)kv_items, cs, a.scale);
   return hipGetLastError();

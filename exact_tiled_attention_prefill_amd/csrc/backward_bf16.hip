@@ -250,7 +250,15 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
     const uint8_t* vl = ring[SL][1];
     const int k0 = t * kBTile;
     if (wave_has_rows && (!CAUSAL || k0 <= wave_last_row)) {
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+      // S^T, and dP^T from -D of the lane's row, so dS^T = P^T dP^T.  The
+      // regions are fenced (sched_barrier) so that each one's grouping hints
+      // see only its own instructions.
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[mb][r] = -dd;
+      // region 1: S^T = K Q^T (the dP^T initialisation runs alongside)
 #pragma unroll
       for (int t2 = 0; t2 < KS; ++t2)
 #pragma unroll
@@ -259,16 +267,32 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
           s[mb] = mfma32x32x16(kf, qf[t2], s[mb]);
         }
 #pragma unroll
-      for (int t2 = 0; t2 < KS; ++t2)
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // region 2: dP^T = V dO^T - D || P^T = exp2(cs S^T - lse log2 e), in
+      // two fenced halves (half the k-steps with one score block's
+      // exponentials each: one group pattern over all of it went unfilled)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + koff[t2] + mb * 32 * D * 2);
-          dp[mb] = mfma32x32x16(vf, df[t2], dp[mb]);
+      for (int hk = 0; hk < 2; ++hk) {
+#pragma unroll
+        for (int t2 = hk * KS / 2; t2 < (hk + 1) * KS / 2; ++t2)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + koff[t2] + mb * 32 * D * 2);
+            dp[mb] = mfma32x32x16(vf, df[t2], dp[mb]);
+          }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[hk][r] = fast_exp2(fmaf(s[hk][r], cs, -l2));
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 32 / KS, 0);
         }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] = fast_exp2(fmaf(s[mb][r], cs, -l2));  // P^T
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (!tile_all_visible(k0)) {
         // key of (mb, r) = k0 + 4hi + 32mb + 8(r/4) + r%4; visible when <= lim
         // (a select, not a product: a masked exponent may be +inf)
@@ -278,15 +302,12 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[mb][r] = 32 * mb + 8 * (r >> 2) + (r & 3) <= lim ? s[mb][r] : 0.f;
       }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] *= dp[mb][r] - dd;  // dS^T
+      // region 3: dQ^T += K^T dS^T || dS^T = P^T dP^T, packed per 16 keys
 #pragma unroll
       for (int ks2 = 0; ks2 < kBTile / 16; ++ks2) {
         float tmp[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j];
+        for (int j = 0; j < 8; ++j) tmp[j] = s[ks2 >> 1][8 * (ks2 & 1) + j] * dp[ks2 >> 1][8 * (ks2 & 1) + j];
         const bf16x8 pf = pack_bf16x8(tmp);
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
@@ -295,6 +316,14 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
           const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
           acc[md] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf, acc[md]);
         }
+      }
+      // the first 16 keys' dS^T and packs, then one matrix product and three
+      // VALU ops per step
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+#pragma unroll
+      for (int i = 0; i < MD * kBTile / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
     }
     if (t + 1 < ntiles) bwait_vmem_le<0>();

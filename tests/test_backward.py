@@ -66,6 +66,20 @@ def test_backward_gqa_and_scale(G, scale):
     check_grad(dv, rv, "dv")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_gqa_long(causal):
+    """Four query heads per key/value head over 1000 rows: the dK/dV kernel's
+    loop over the group's heads crosses many unmasked interior tiles of each
+    head, the causal diagonal and the ragged end."""
+    print(f"backward gqa long causal={causal}", flush=True)
+    q, k, v, do, scale = I.backward_inputs(1, 8, 2, 1000, 128, seed=40 + causal)
+    dq, dk, dv = run_backward(q, k, v, do, causal, scale, workspace=True)
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, causal, scale)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
 def test_backward_deterministic():
     q, k, v, do, scale = I.backward_inputs(1, 4, 2, 257, 128, seed=3)
     a = run_backward(q, k, v, do, True, scale)

@@ -20,10 +20,12 @@
 // gfx950 design:
 //   * Workgroup = 4 waves = 128 query rows of one head; two workgroups share
 //     a CU, so every SIMD runs two waves from different workgroups whose
-//     softmax (VALU) and matrix products (MFMA) interleave.  Wave w owns rows
-//     q0 + w + 4j (j = 0..31): interleaving the rows gives every wave the same
-//     causal work, so the per-tile barrier never waits on a wave with more
-//     tiles.  Q stays in VGPRs.
+//     softmax (VALU) and matrix products (MFMA) interleave.  Rows that see
+//     8K keys or more on average use 8 waves = 256 rows instead (one
+//     workgroup per CU, half the K/V copies per row).  Wave w of W owns rows
+//     q0 + w + Wj (j = 0..31): interleaving the rows gives every wave the
+//     same causal work, so the per-tile barrier never waits on a wave with
+//     more tiles.  Q stays in VGPRs.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query per
 //     32-key block, so row max and row sum are in-lane plus one
@@ -59,26 +61,27 @@
 //     streams about n+1 key-tile pairs.
 #include "common.h"
 #include "kernels.h"
+#include <algorithm>
 #include <type_traits>
 
 namespace fa {
 namespace {
 
-// Launch shape (compile-time): waves per workgroup and keys per tile.  Both
-// alternatives pass the same parity tests.  Eight waves (256 query rows
-// sharing each K/V tile) halve the L2 -> LDS traffic and gain 1-2% from 8K
-// keys on, but lose at 1K-4K causal, where one workgroup per CU leaves its
-// prologue and the wider causal diagonal exposed; 32-key tiles are ~3%
-// slower.
+// Launch shape: waves per workgroup (a template parameter, 4 or 8) and keys
+// per tile (compile-time).  Eight waves (256 query rows sharing each K/V
+// tile, one workgroup per CU) halve the L2 -> LDS traffic and gain 1-3% when
+// the average query row sees 8K keys or more, but lose 3-11% on shorter rows
+// (causal 1K-8K, 1K-key windows), where one workgroup per CU leaves its
+// prologue and the wider causal diagonal exposed.  The launcher picks the
+// width per call (FA_PREFILL_WAVES=4 or 8 forces one, for testing).  32-key
+// tiles are ~3% slower.
 #ifndef FA_PREFILL_WAVES
-#define FA_PREFILL_WAVES 4
+#define FA_PREFILL_WAVES 0
 #endif
 #ifndef FA_PREFILL_BC
 #define FA_PREFILL_BC 64
 #endif
-constexpr int kWaves = FA_PREFILL_WAVES;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBR = 32 * kWaves;       // query rows per workgroup
+static_assert(FA_PREFILL_WAVES == 0 || FA_PREFILL_WAVES == 4 || FA_PREFILL_WAVES == 8, "waves: 0 (choose), 4 or 8");
 constexpr int kBC = FA_PREFILL_BC;     // keys per tile (64, or 32)
 constexpr int kMB = kBC / 32;          // 32-key MFMA blocks per tile
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
@@ -132,12 +135,15 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* l
 
 // VARLEN: packed variable-length sequences (VarlenRef); N is then the longest
 // sequence's query count, which sizes the grid.
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
+template <int D, bool CAUSAL, bool VARLEN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int Hq, int Hkv, int N, int n_qtiles, int n_items, int block_heads, float c, uint32_t qflip,
     VarlenRef vr) {
+  constexpr int kWaves = WAVES;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kBR = 32 * kWaves;          // query rows per workgroup
   constexpr int KS = D / 16;                // k-steps of S^T = K Q^T
   constexpr int MD = D / 32;                // 32-row blocks of O^T
   constexpr int RC = D / 8;                 // 16-byte chunks per row
@@ -514,23 +520,47 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_bf16_kernel(
 // N 1K..16K: within 1% of the best block size at every length).
 int block_heads_for(int n_slots) { return n_slots < 16 ? 4 : 1; }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, int WAVES>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int kBR = 32 * WAVES;  // query rows per workgroup
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const int n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // causal slots pair two query tiles
   const long long items = (long long)n_slots * a.B * a.Hq;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int block_heads = block_heads_for(n_slots);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)items), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN, WAVES>), dim3((unsigned)items), dim3(64 * WAVES), 0,
+                     stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
                      a.N, n_qtiles, (int)items, block_heads, a.c, a.neg ? 0x80008000u : 0u, a.varlen);
   return hipGetLastError();
 }
 
+// Eight waves when the average query row sees at least 8192 keys (d = 128;
+// the wider workgroup was measured there only).  Dense rows see N keys, or
+// (N + 1) / 2 on average under the causal mask.  Packed sequences of average
+// lengths Lq = total_q / B, Lk = total_k / B see Lk keys, or Lk - (Lq - 1) / 2
+// under the bottom-right causal mask (the dense value for one full-length
+// sequence, so both entry points pick the same width and agree bit for bit);
+// a window caps them at window_left + 1.
+bool wide_launch(const PrefillArgs& a) {
+  if (FA_PREFILL_WAVES != 0) return FA_PREFILL_WAVES == 8;
+  if (a.d != 128 || a.B <= 0) return false;
+  double keys;
+  if (a.varlen.cu_q != nullptr) {
+    keys = (double)a.varlen.total_k / a.B - (a.causal ? 0.5 * ((double)a.varlen.total_q / a.B - 1.0) : 0.0);
+    if (a.varlen.window >= 0) keys = std::min(keys, (double)a.varlen.window + 1);
+  } else {
+    keys = a.causal ? 0.5 * ((double)a.N + 1) : (double)a.N;
+  }
+  return keys >= 8192.0;
+}
+
 template <int D, bool VARLEN>
 hipError_t launch_c(const PrefillArgs& a, hipStream_t stream) {
-  return a.causal ? launch<D, true, VARLEN>(a, stream) : launch<D, false, VARLEN>(a, stream);
+  if (wide_launch(a))
+    return a.causal ? launch<D, true, VARLEN, 8>(a, stream) : launch<D, false, VARLEN, 8>(a, stream);
+  return a.causal ? launch<D, true, VARLEN, 4>(a, stream) : launch<D, false, VARLEN, 4>(a, stream);
 }
 
 }  // namespace

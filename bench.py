@@ -57,6 +57,16 @@ def varlen_pairs(lens, causal, window):
     return total
 
 
+def prefill_waves(d, causal, n_q, n_k, window=-1):
+    """Waves per prefill workgroup that the library's launcher picks (for
+    the kernel labels): 8 when the average query row of sequences with n_q
+    queries against n_k keys sees 8192 keys or more at d = 128, else 4."""
+    keys = n_k - ((n_q - 1) / 2 if causal else 0)
+    if window >= 0:
+        keys = min(keys, window + 1)
+    return 8 if d == 128 and keys >= 8192 else 4
+
+
 def prefill_bytes(B, Hq, Hkv, N, d, elem=2):
     return (2 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
 
@@ -389,7 +399,9 @@ def main():
         flops = 4 * 128 * hq * varlen_pairs(lens, causal, window)
         cfg = {"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128, "causal": causal,
                "window_left": window}
-        vl_legs.append((name, vf, flops, cfg))
+        waves = prefill_waves(128, causal, sum(nq for nq, _ in lens) / len(lens),
+                              sum(nk for _, nk in lens) / len(lens), window)
+        vl_legs.append((name, vf, flops, cfg, f"prefill_bf16_kernel<128,causal,varlen,{waves} waves>"))
 
     if run_bwd:
         # backward of the MHA 4K causal workload: the forward's o and lse feed it
@@ -404,10 +416,10 @@ def main():
                              workspace=bws)
         vl_legs.append(("backward", bwf, 2.5 * prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True),
                         {"workload": pc.name, "flops": "2.5 x forward (five matrix products per score)",
-                         "kernels": "dQ (with the D and lse rows) + dK/dV"}))
+                         "kernels": "dQ (with the D and lse rows) + dK/dV"}, "bwd_dq + bwd_dkdv"))
 
     for _ in range(args.warmup):
-        for _, vf, _, _ in vl_legs:
+        for _, vf, _, _, _ in vl_legs:
             vf()
         if run_prefill:
             pf()
@@ -423,7 +435,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        for j, (_, vf, _, _) in enumerate(vl_legs):
+        for j, (_, vf, _, _, _) in enumerate(vl_legs):
             ev[i][4 + j].record(stream)
             vf()
         ev[i][0].record(stream)
@@ -479,7 +491,8 @@ def main():
                              "tflops": tflops, "tokens_per_s": pc.B * pc.N / (p_avg * 1e-3),
                              "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": F}
         traffic = measured_traffic("prefill_bf16_mha4k_counters", PREFILL_SRC)
-        result["roofline"] = {"kernel": "prefill_bf16_kernel<128,causal>", "bound": "mfma",
+        result["roofline"] = {"kernel": f"prefill_bf16_kernel<128,causal,{prefill_waves(pc.d, True, pc.N, pc.N)} waves>",
+                              "bound": "mfma",
                               "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                               "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                               "algorithmic_bytes": prefill_bytes(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d),
@@ -502,13 +515,12 @@ def main():
                             "device_memory": d_mem}
         if result["value"] is None:
             result["value"], result["unit"] = gbs, "GB/s"
-    for (name, _, flops, cfg), ms in zip(vl_legs, vl_ms):
+    for (name, _, flops, cfg, kernel), ms in zip(vl_legs, vl_ms):
         avg = sum(ms) / K
         tf = flops / (avg * 1e-3) / 1e12
         result[name] = {"config": cfg, "ms_avg": avg, "ms_median": ms[K // 2], "ms_min": ms[0], "tflops": tf,
                         "flops_per_launch": flops,
-                        "roofline": {"kernel": ("bwd_dq + bwd_dkdv" if name == "backward"
-                                                else "prefill_bf16_kernel<128,causal,varlen>"), "bound": "mfma",
+                        "roofline": {"kernel": kernel, "bound": "mfma",
                                      "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                      "frac": tf / PEAK_BF16_TFLOPS}}
         if result["value"] is None:
@@ -553,7 +565,8 @@ def main():
         result[name] = {"workload": cfg.name, "steps": steps, "ms_avg": avg, "ms_median": ms[steps // 2],
                         "ms_min": ms[0], "tflops": tf, "tokens_per_s": cfg.B * cfg.N / (avg * 1e-3),
                         "flops_per_launch": F,
-                        "roofline": {"kernel": "prefill_bf16_kernel<128,causal>", "bound": "mfma", "achieved": tf,
+                        "roofline": {"kernel": f"prefill_bf16_kernel<128,causal,{prefill_waves(cfg.d, True, cfg.N, cfg.N)} waves>",
+                                     "bound": "mfma", "achieved": tf,
                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}
         cfg_legs.append(name)
         del cqd, ckd_, cvd, cod, cld
@@ -565,7 +578,7 @@ def main():
         result["ceilings"] = ceil
         if ceil is not None:
             sus = ceil["mfma_bf16_random_operands"]["tflops"]
-            for rl in ([result.get("roofline")] + [result[n]["roofline"] for n, _, _, _ in vl_legs]
+            for rl in ([result.get("roofline")] + [result[n]["roofline"] for n, _, _, _, _ in vl_legs]
                        + [result[n]["roofline"] for n in cfg_legs]):
                 if rl is not None:
                     rl["measured_ceiling"] = sus

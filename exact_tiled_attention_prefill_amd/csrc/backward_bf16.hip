@@ -16,7 +16,9 @@
 //          copies never leave it).  Key tiles then stream through an LDS ring;
 //          per 64-key tile and wave S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
 //          then dQ^T += K^T dS^T, with dS^T packed to bf16 straight from the
-//          accumulator layout into the B operand (48 MFMAs);
+//          accumulator layout into the B operand (48 MFMAs).  dP^T starts at
+//          -D, the exponentials run under the dP^T products and dS^T under
+//          the dQ^T products;
 //   dK/dV: one workgroup of 8 waves per 128 keys of one key/value head,
 //          looping over the group's query heads and their 64-row query
 //          tiles.  Waves w and w+4 own the same 32 keys and split each tile's
@@ -27,10 +29,13 @@
 //          product, and the exponentials (and dS) run under the dP (and dV)
 //          matrix products.  No atomics: every output element has
 //          one writer, so results are deterministic.
+// In both kernels the per-element causal / end-of-sequence mask runs only on
+// tiles that some row of the wave does not see in full, and the tile loops
+// are unrolled by two so that ring slots are immediates.
 // Q, dO (dK/dV kernel) and K (dQ kernel) are read from LDS both row-wise
 // (ds_read_b128) and transposed (ds_read_b64_tr_b16); their 16-byte chunks
 // use one XOR swizzle that leaves both access patterns free of bank
-// conflicts.
+// conflicts (dQ's V tile, read row-wise only, shares it).
 #include "common.h"
 #include "kernels.h"
 #include <type_traits>

@@ -27,6 +27,12 @@
 //       and accumulates pairs of keys with v_dot2_f32_bf16 against bf16
 //       probabilities.  Each wave keeps its own running max / sum (lazy
 //       rescale); the four waves are merged once per chunk through LDS.
+//     GQA groups of 8 or more query heads (multiples of 8) use a matrix-core
+//       variant instead: the dot2 work grows with the heads a workgroup
+//       serves and saturates the VALU from 8 heads on.  There each wave
+//       streams its own 32-key tiles through a private LDS ring and computes
+//       S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with up to
+//       32 heads as the columns (the prefill kernel's layouts).
 //     Each (sequence, head) row's chunk order is rotated by the row index so
 //     that the XCDs receive equal shares of real chunks.
 //     fp32 path (512-key chunks): VGPR loads and fp32 FMAs, 4 lanes per row
@@ -473,9 +479,7 @@ __device__ __forceinline__ float dpp_f(float a) {
 // grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
 // PAGED: kc / vc are page pools and pg maps logical pages to pool pages.
 template <int D, int GT, bool PAGED>
-// Eight query heads per workgroup at d = 128 need more than the 128 VGPRs of
-// four workgroups per CU; three workgroups per CU avoid spilling.
-__global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
+__global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
     int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg) {
@@ -750,8 +754,241 @@ __global__ __launch_bounds__(256, (GT >= 8 && D >= 128) ? 3 : FA_DEC_MINBLOCKS) 
   }
 }
 
-// Query heads per bf16 split workgroup for a GQA group of G heads.
-int bf16_group_tile(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
+// ---------------------------------------------------------------------------
+// bf16 split kernel for GQA groups of 8 or more query heads: matrix cores.
+// The per-key work grows with the heads a workgroup serves; on the VALU (dot2)
+// it saturates from 8 heads on (4.9 TB/s at 8, 2.6 TB/s at 16).  Here
+// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with the
+// GM heads as the 32 columns (unused columns hold zero queries; the matrix
+// cores have ample headroom at HBM speed).  Each wave streams its own 32-key
+// tiles (tiles w, w+4, ... of the chunk) through a private two-slot LDS ring,
+// so no barrier runs per tile; the four waves' (m, l, o) are merged once per
+// chunk.  The register and LDS layouts are those of the prefill kernel: K rows
+// read with ds_read_b128 from 16-byte chunks XOR-swizzled by row, V read
+// transposed with ds_read_b64_tr_b16, P packed from the accumulator into the B
+// operand, a lazily rescaled running max per head.
+template <int D>
+__device__ __forceinline__ int mk_swz(int row) {  // K: 16 rows x one chunk per read
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int mv_swz(int row) {  // V: 4 rows x 4 chunks per transposed read
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+template <int D, int GM, bool PAGED>
+__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg) {
+  constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
+  constexpr int MD = D / 32;        // 32-row blocks of O^T
+  constexpr int RC = D / 8;         // 16-byte chunks per cache row
+  constexpr int TILE = 32 * D * 2;  // bytes per 32-key K (or V) tile
+  constexpr int RPI = 64 / RC;      // rows per copy instruction (a wave moves 1 KB)
+  constexpr int NCP = 32 / RPI;     // copy instructions per K (or V) tile
+  static_assert(GM == 8 || GM == 16 || GM == 32, "heads per workgroup");
+  // [wave][slot][K, V]; after the key loop it holds the waves' outputs
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][2][TILE];
+  __shared__ float m_w[4][GM], l_w[4][GM];
+  __shared__ int pid_lds[PAGED ? kMaxChunkPages : 1];
+  static_assert(4 * GM * D * 4 <= 4 * 2 * 2 * TILE, "wave outputs must fit in the ring");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int x = lane & 31;
+  const int hi = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int split = split_of_block(nsplit);
+  const int G = Hq / Hkv;
+  const int slices = G / GM;
+  const int kvh = blockIdx.y / slices;
+  const int h0 = kvh * G + (blockIdx.y % slices) * GM;
+  const int b = blockIdx.z;
+
+  const int L = min(max(seqlens[b], 0), maxlen);
+  const int kbeg = split * chunk;
+  if (kbeg >= L) return;
+  const int n = min(chunk, L - kbeg);
+  const int ntile = (n + 31) / 32;
+  const size_t cbase = PAGED ? 0 : (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(kc + cbase);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(vc + cbase);
+  // paged: this chunk's slice of the block table, pool ids clamped into the
+  // pool so that a bad table can never address outside it
+  const int slot0 = PAGED ? (kbeg >> pg.page_shift) : 0;
+  if (PAGED) {
+    const int nslots = ((kbeg + n - 1) >> pg.page_shift) - slot0 + 1;  // <= kMaxChunkPages
+    if (tid < nslots)
+      pid_lds[tid] = min(max(pg.block_table[(size_t)b * pg.max_pages + slot0 + tid], 0), pg.num_pages - 1);
+    __syncthreads();
+  }
+
+  // Q^T fragments (B operand): column x = head h0 + x (zero past GM),
+  // d = 16ks + 8hi + 0..7.  Used at once, so their loads are waited for here
+  // and not inside the key loop (where the counter also sees the copies).
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qr = q + ((size_t)b * Hq + h0 + min(x, GM - 1)) * D + hi * 8;
+    u32x4 w[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u32x4*>(qr + ks * 16);
+    const uint32_t keep = x < GM ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (w[ks] ^ qflip) & keep);
+  }
+  // LDS read offsets within a tile: K row x, chunk (2ks + hi); V^T rows
+  // 4hi + (i>>2) (+8, +16ks2), chunk of column block md
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = x * (D * 2) + (((2 * ks + hi) ^ mk_swz<D>(x)) << 4);
+  int voff[MD];
+  {
+    const int i = lane & 15;
+    const int row = 4 * hi + (i >> 2);
+    const int colc = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) voff[md] = row * (D * 2) + (((4 * md + colc) ^ mv_swz<D>(row)) << 4) + 8 * (i & 1);
+  }
+
+  // Copy instruction i of a tile moves rows RPI*i .. RPI*i + RPI - 1: lane l
+  // fills physical chunk l % RC of row RPI*i + l / RC, which holds logical
+  // chunk (l % RC) ^ swz(row).  Rows past the chunk end re-read its last key
+  // (never past it: the cache there may hold anything); their scores are
+  // masked.
+  const int crow = lane / RC, ccp = lane % RC;
+  const int pmask = PAGED ? (1 << pg.page_shift) - 1 : 0;
+  auto issue = [&](int t, int slot) {
+    uint8_t* kl = &ring[wave_s][slot][0][0];
+    uint8_t* vl = &ring[wave_s][slot][1][0];
+    const int r0 = 32 * t;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int row = RPI * i + crow;
+      const int rs = min(row, n - 1 - r0);
+      const uint32_t kch = (uint32_t)((ccp ^ mk_swz<D>(row)) << 4);
+      const uint32_t vch = (uint32_t)((ccp ^ mv_swz<D>(row)) << 4);
+      if (PAGED) {
+        const int key = kbeg + r0 + rs;
+        const int pid = pid_lds[(key >> pg.page_shift) - slot0];
+        const size_t rb = ((((size_t)pid * Hkv + kvh) << pg.page_shift) | (size_t)(key & pmask)) * (D * 2);
+        dec_dma16_addr(kp + rb + kch, kl + i * 1024);
+        dec_dma16_addr(vp + rb + vch, vl + i * 1024);
+      } else {
+        dec_dma16(kp + (size_t)r0 * D * 2, (uint32_t)(rs * D * 2) + kch, kl + i * 1024);
+        dec_dma16(vp + (size_t)r0 * D * 2, (uint32_t)(rs * D * 2) + vch, vl + i * 1024);
+      }
+    }
+  };
+
+  f32x16 oacc[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) oacc[md] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int myn = ntile > wave_s ? (ntile - 1 - wave_s) / 4 + 1 : 0;  // tiles w, w+4, ... of the chunk
+  if (myn > 0) issue(wave_s, 0);
+  for (int j = 0; j < myn; ++j) {
+    const int t = wave_s + 4 * j;
+    const int slot = j & 1;
+    if (j + 1 < myn) {
+      issue(t + 4, slot ^ 1);      // that slot's reads (tile j-1) finished at its end
+      dec_wait_vmem_le<2 * NCP>();  // tile j landed; tile j+1 may be in flight
+    } else {
+      dec_wait_vmem_le<0>();
+    }
+    const uint8_t* kl = &ring[wave_s][slot][0][0];
+    const uint8_t* vl = &ring[wave_s][slot][1][0];
+    // S^T = K Q^T: lane (x, hi) holds keys 8(r/4) + 4hi + r%4 of the tile for head x
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kl + koff[ks]), qf[ks], s);
+    const int k0 = 32 * t;
+    if (k0 + 32 > n) {
+      const int lim = n - 1 - k0 - 4 * hi;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[r];
+    }
+    // running max per head (lazy rescale against a stale max, as in prefill)
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = max_halves(mx) * c;  // -inf stays -inf (c > 0)
+    if (__any(mx > m_run + kTauB)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);  // 0 on the first tile (m_run = -inf, mn finite)
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) oacc[md] *= alpha;
+      m_run = mn;
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      float tmp[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float p = fast_exp2(fmaf(s[8 * ks2 + jj], c, -m_run));
+        l_run += p;
+        tmp[jj] = p;
+      }
+      pf[ks2] = pack_bf16x8(tmp);
+    }
+    // O^T += V^T P^T over the tile's two 16-key steps
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const u32x2 a0 = dec_read_tr(vl + voff[md] + (16 * ks2) * D * 2);
+        const u32x2 a1 = dec_read_tr(vl + voff[md] + (16 * ks2 + 8) * D * 2);
+        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+        oacc[md] = mfma32x32x16(__builtin_bit_cast(bf16x8, a), pf[ks2], oacc[md]);
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot may be refilled next
+  }
+
+  // ---- merge the four waves' (m, l, o) through the ring ----
+  const float lt = sum_halves(l_run);
+  __syncthreads();  // every copy landed and every read finished: the ring is free
+  float(&o_w)[4][GM][D] = *reinterpret_cast<float(*)[4][GM][D]>(&ring[0][0][0][0]);
+  if (x < GM) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o_w[wave_s][x][32 * md + 8 * (r >> 2) + 4 * hi + (r & 3)] = oacc[md][r];
+    if (hi == 0) {
+      m_w[wave_s][x] = m_run;  // -inf for a wave without tiles (then l = 0, o = 0)
+      l_w[wave_s][x] = lt;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GM * D; i += 256) {
+    const int g = i / D, d = i % D;
+    float M = m_w[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, m_w[w][g]);
+    float l = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(m_w[w][g] - M);  // 0 for a wave that saw no key
+      l = fmaf(l_w[w][g], f, l);
+      a = fmaf(o_w[w][g][d], f, a);
+    }
+    const size_t pidx = ((size_t)b * Hq + h0 + g) * nsplit + split;
+    part_o[pidx * D + d] = a / l;
+    if (d == 0) part_lse[pidx] = M * kLn2 + __logf(l);
+  }
+}
+
+// Query heads per bf16 split workgroup for a GQA group of G heads: groups of
+// 8 or more (multiples of 8) run on the matrix-core kernel with up to 32 heads
+// per workgroup; smaller ones on the VALU kernel with 4, 2 or 1.
+bool bf16_uses_mfma(int G) { return G % 8 == 0; }
+int bf16_group_tile(int G) {
+  if (bf16_uses_mfma(G)) return G % 32 == 0 ? 32 : G % 16 == 0 ? 16 : 8;
+  return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+}
 
 // Keys per bf16 split workgroup: the largest of 2048, 1024, 512, 256 that
 // still gives at least two full rounds of resident workgroups (4 per CU on
@@ -790,10 +1027,34 @@ hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int GM, bool PAGED>
+hipError_t launch_bf16_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
+  const int nsplit = (a.maxlen + chunk - 1) / chunk;
+  const int G = a.Hq / a.Hkv;
+  float* part_o = static_cast<float*>(a.ws);
+  const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
+  dim3 g1(nsplit, a.Hkv * (G / GM), a.B);
+  if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_bf16_mfma_kernel<D, GM, PAGED>), g1, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
+                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u, a.paged);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
+                     part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, chunk);
+  return hipGetLastError();
+}
+
 template <int D, bool PAGED>
 hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
   switch (bf16_group_tile(a.Hq / a.Hkv)) {
-    case 8: return launch_bf16<D, 8, PAGED>(a, stream);
+    case 32: return launch_bf16_mfma<D, 32, PAGED>(a, stream);
+    case 16: return launch_bf16_mfma<D, 16, PAGED>(a, stream);
+    case 8: return launch_bf16_mfma<D, 8, PAGED>(a, stream);
     case 4: return launch_bf16<D, 4, PAGED>(a, stream);
     case 2: return launch_bf16<D, 2, PAGED>(a, stream);
     default: return launch_bf16<D, 1, PAGED>(a, stream);

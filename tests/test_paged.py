@@ -42,7 +42,7 @@ def run_contiguous(q, kc, vc, lens, scale):
 
 @pytest.mark.parametrize("page", [16, 32, 64, 256, 2048])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 32])
 def test_paged_decode_matches_oracle(page, d, G):
     lens = [0, 1, 15, 16, 17, 511, 1024, 1025, 2000, 2048, 7]
     print(f"paged decode page={page} d={d} G={G}", flush=True)

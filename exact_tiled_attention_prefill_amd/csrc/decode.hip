@@ -15,24 +15,18 @@
 //     memory requirements for inference in large language models", GQA
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
-//     bf16 path (chunks of 2048, 1024, 512 or 256 keys, the largest that keeps
-//       two rounds of resident workgroups busy): the chunk streams through a
-//       ring of 32-key K/V tiles copied HBM -> LDS by global_load_lds_dwordx4
-//       (no VGPR staging).  The ring is only two stages deep so that four
-//       workgroups (16 waves) fit per CU: on MI355X the number of resident
-//       workgroups hides the per-tile dependency chain better than a deeper
-//       ring does.  Scores use 8 lanes per key and v_dot2_f32_bf16 (two bf16
-//       products per instruction, no widening); values are read with the
-//       transposing ds_read_b64_tr_b16 so each lane owns fixed output columns
-//       and accumulates pairs of keys with v_dot2_f32_bf16 against bf16
-//       probabilities.  Each wave keeps its own running max / sum (lazy
-//       rescale); the four waves are merged once per chunk through LDS.
-//     GQA groups of 8 or more query heads (multiples of 8) use a matrix-core
-//       variant instead: the dot2 work grows with the heads a workgroup
-//       serves and saturates the VALU from 8 heads on.  There each wave
-//       streams its own 32-key tiles through a private LDS ring and computes
-//       S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with up to
-//       32 heads as the columns (the prefill kernel's layouts).
+//     bf16 path (chunks of 2048, 1024, 512 or 256 keys, the largest that
+//       still gives 2048 workgroups): one workgroup serves the whole GQA group
+//       (up to 32 query heads).  Each of its four waves streams its own
+//       32-key tiles of the chunk through a private two-slot LDS ring, copied
+//       HBM -> LDS by global_load_lds_dwordx4 (no VGPR staging, no per-tile
+//       barrier), and computes S^T = K Q^T and O^T += V^T P^T on
+//       v_mfma_f32_32x32x16_bf16 with the group's heads as the columns -- the
+//       prefill kernel's register and LDS layouts.  The products cost the same
+//       per key whatever the number of heads, so the group's K/V is read once
+//       and the matrix cores stay far below their rate at HBM speed.  Each
+//       wave keeps its own running max / sum per head (lazy rescale); the
+//       four waves are merged once per chunk through LDS.
 //     Each (sequence, head) row's chunk order is rotated by the row index so
 //     that the XCDs receive equal shares of real chunks.
 //     fp32 path (512-key chunks): VGPR loads and fp32 FMAs, 4 lanes per row
@@ -413,29 +407,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel: DMA ring + dot2.
-#ifndef FA_DEC_PASSES
-#define FA_DEC_PASSES 1
-#endif
-#ifndef FA_DEC_RING
-#define FA_DEC_RING 2
-#endif
-#ifndef FA_DEC_MINBLOCKS
-#define FA_DEC_MINBLOCKS 4
-#endif
-constexpr int kPasses = FA_DEC_PASSES;           // 32-key passes per ring stage
-constexpr int kStageKeys = 32 * kPasses;         // keys per ring stage
-constexpr int kRingB = FA_DEC_RING;              // ring stages (kRingB - 1 in flight ahead of compute)
+// bf16 split kernel helpers.
 constexpr float kTauB = 8.0f;   // lazy-rescale threshold (log2 units)
 
 template <int n>
 __device__ __forceinline__ void dec_wait_vmem_le() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-}
-__device__ __forceinline__ void dec_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 // lane l's 16 bytes from base + off land at lds_wave_base + 16*l (inline asm:
 // the compiler does not track it; completion is ordered by vmcnt + barrier).
@@ -460,314 +437,20 @@ __device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
   typedef __attribute__((address_space(3))) dec_i16x4 lds_t;
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_t*)(p)));
 }
-// Order LDS traffic between lanes of one wave: data written by some lanes is
-// read by others (and later overwritten), which without this is a data race
-// the compiler may exploit (e.g. by sinking the read into the writers' branch).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float a) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), CTRL, 0xF, 0xF, false));
-}
-
-// grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
-// PAGED: kc / vc are page pools and pg maps logical pages to pool pages.
-template <int D, int GT, bool PAGED>
-__global__ __launch_bounds__(256, FA_DEC_MINBLOCKS) void decode_bf16_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg) {
-  constexpr int RC = D / 8;                         // 16-byte chunks per cache row
-  constexpr int STAGE = kStageKeys * D * 2;         // bytes per K (or V) stage
-  constexpr int CPT = kStageKeys * RC / 256;        // DMA chunks per thread per K (or V) stage
-  constexpr int DMA_PER_STAGE = 2 * CPT;
-  constexpr int EPL = D / 8;                        // score phase: elements per lane (8 lanes/key)
-  constexpr int NCB = D / 64;                       // value phase: 64-column blocks
-  static_assert(CPT >= 1 && CPT * 256 == kStageKeys * RC, "stage must split evenly");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingB][2][STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][GT][8];
-  __shared__ float m_w[4][GT], l_w[4][GT];
-  __shared__ int pid_lds[PAGED ? kMaxChunkPages : 1];
-  static_assert(4 * GT * D * 4 <= kRingB * 2 * STAGE, "wave partials must fit in the ring");
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int split = split_of_block(nsplit);
-  const int G = Hq / Hkv;
-  const int slices = G / GT;
-  const int kvh = blockIdx.y / slices;
-  const int h0 = kvh * G + (blockIdx.y % slices) * GT;
-  const int b = blockIdx.z;
-
-  const int L = min(max(seqlens[b], 0), maxlen);
-  const int kbeg = split * chunk;
-  if (kbeg >= L) return;
-  const int n = min(chunk, L - kbeg);
-  const int nst = (n + kStageKeys - 1) / kStageKeys;
-  const size_t cbase = PAGED ? 0 : (((size_t)b * Hkv + kvh) * maxlen + kbeg) * D;
-  const uint8_t* kp = reinterpret_cast<const uint8_t*>(kc + cbase);
-  const uint8_t* vp = reinterpret_cast<const uint8_t*>(vc + cbase);
-  // paged: this chunk's slice of the block table, pool ids clamped into the
-  // pool so that a bad table can never address outside it
-  const int slot0 = PAGED ? (kbeg >> pg.page_shift) : 0;
-  if (PAGED) {
-    const int nslots = ((kbeg + n - 1) >> pg.page_shift) - slot0 + 1;  // <= kMaxChunkPages
-    if (tid < nslots)
-      pid_lds[tid] = min(max(pg.block_table[(size_t)b * pg.max_pages + slot0 + tid], 0), pg.num_pages - 1);
-    __syncthreads();
-  }
-
-  // ---- score layout: key kk = lane/8 of the wave's 8 keys, part j = lane%8 (EPL elements) ----
-  const int kk = lane >> 3;
-  const int j = lane & 7;
-  uint32_t qv[GT][EPL / 2];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    const uint32_t* qr = reinterpret_cast<const uint32_t*>(q + ((size_t)b * Hq + h0 + g) * D + j * EPL);
-#pragma unroll
-    for (int e = 0; e < EPL / 2; e += 4) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qr + e);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) qv[g][e + t] = w[t] ^ qflip;
-    }
-  }
-  // K LDS reads: row 8*wave + kk, logical chunks j*EPL/8 .. (row-major, chunk ^ (row & 1) for D=128)
-  const int krow = 8 * wave + kk;
-  int kofs[EPL / 8];
-#pragma unroll
-  for (int e = 0; e < EPL / 8; ++e) {
-    const int ch = j * (EPL / 8) + e;
-    kofs[e] = krow * D * 2 + ((D == 128 ? (ch ^ (krow & 1)) : ch) << 4);
-  }
-  // V transposing reads: lane i of 16-lane group gm reads row 8*wave + 4kq + (i>>2),
-  // columns 64cb + 16gm + 4(i&3) .. +3; it receives column 64cb + lane for 4 keys.
-  int vofs[NCB];
-  {
-    const int i = lane & 15, gm = lane >> 4;
-    const int vrow = 8 * wave + (i >> 2);
-    const int vsw = D == 128 ? 4 * (vrow & 3) : 4 * ((vrow >> 1) & 1);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int ch = (64 * cb + 16 * gm + 4 * (i & 3)) >> 3;
-      vofs[cb] = vrow * D * 2 + ((ch ^ vsw) << 4) + 8 * (i & 1);
-    }
-  }
-  // DMA: chunk p = i*256 + tid of a stage: row p / RC, chunk p % RC (swizzled like the reads)
-  uint32_t dk[CPT], dv[CPT];
-  int drow[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int p = i * 256 + tid;
-    const int r = p / RC, cp = p % RC;
-    drow[i] = r;
-    const int ksw = D == 128 ? (cp ^ (r & 1)) : cp;
-    const int vsw = D == 128 ? (cp ^ (4 * (r & 3))) : (cp ^ (4 * ((r >> 1) & 1)));
-    dk[i] = (uint32_t)(r * D * 2 + (ksw << 4));
-    dv[i] = (uint32_t)(r * D * 2 + (vsw << 4));
-  }
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int st) {
-    const int r0 = st * kStageKeys;
-    const uint8_t* kb = kp + (size_t)r0 * D * 2;
-    const uint8_t* vb = vp + (size_t)r0 * D * 2;
-    uint8_t* kl = ring[st % kRingB][0];
-    uint8_t* vl = ring[st % kRingB][1];
-    if (PAGED) {
-      // row r of the stage is cache entry kbeg + r0 + r (the last valid entry
-      // for rows past the end): pool page, then the row within the page
-      const int pmask = (1 << pg.page_shift) - 1;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int key = kbeg + r0 + min(drow[i], n - 1 - r0);
-        const int pid = pid_lds[(key >> pg.page_shift) - slot0];
-        const size_t row = ((((size_t)pid * Hkv + kvh) << pg.page_shift) | (size_t)(key & pmask)) * (D * 2);
-        dec_dma16_addr(kp + row + (dk[i] - drow[i] * D * 2), kl + (i * 256 + wave_s * 64) * 16);
-        dec_dma16_addr(vp + row + (dv[i] - drow[i] * D * 2), vl + (i * 256 + wave_s * 64) * 16);
-      }
-    } else if (r0 + kStageKeys <= n) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        dec_dma16(kb, dk[i], kl + (i * 256 + wave_s * 64) * 16);
-        dec_dma16(vb, dv[i], vl + (i * 256 + wave_s * 64) * 16);
-      }
-    } else {
-      // rows past the sequence end re-read its last row (never past it: the
-      // cache there may hold anything); their scores are masked below
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int delta = (min(drow[i], n - 1 - r0) - drow[i]) * D * 2;
-        dec_dma16(kb, dk[i] + delta, kl + (i * 256 + wave_s * 64) * 16);
-        dec_dma16(vb, dv[i] + delta, vl + (i * 256 + wave_s * 64) * 16);
-      }
-    }
-  };
-  auto wait_stage = [&](int st) {  // stage st landed; later ones may be in flight
-    const int after = min(kRingB - 2, nst - 1 - st);
-    static_assert(kRingB >= 2 && kRingB <= 6, "ring depth");
-    if (kRingB >= 6 && after >= 4)
-      dec_wait_vmem_le<4 * DMA_PER_STAGE>();
-    else if (kRingB >= 5 && after >= 3)
-      dec_wait_vmem_le<3 * DMA_PER_STAGE>();
-    else if (kRingB >= 4 && after >= 2)
-      dec_wait_vmem_le<2 * DMA_PER_STAGE>();
-    else if (kRingB >= 3 && after >= 1)
-      dec_wait_vmem_le<DMA_PER_STAGE>();
-    else
-      dec_wait_vmem_le<0>();
-  };
-
-  float m_run[GT], l_part[GT], oacc[GT][NCB];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m_run[g] = -INFINITY;
-    l_part[g] = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] = 0.f;
-  }
-
-#pragma unroll
-  for (int st = 0; st < kRingB - 1; ++st)
-    if (st < nst) issue(st);
-  wait_stage(0);
-  dec_barrier();
-
-  for (int st = 0; st < nst; ++st) {
-    if (st + kRingB - 1 < nst) issue(st + kRingB - 1);
-    const uint8_t* kl = ring[st % kRingB][0];
-    const uint8_t* vl = ring[st % kRingB][1];
-#pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-      // ---- scores of this wave's 8 keys for GT heads ----
-      uint32_t kw[EPL / 2];
-  #pragma unroll
-      for (int e = 0; e < EPL / 8; ++e) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kl + kofs[e] + 32 * pass * D * 2);
-  #pragma unroll
-        for (int t = 0; t < 4; ++t) kw[4 * e + t] = w[t];
-      }
-      const bool valid = st * kStageKeys + 32 * pass + krow < n;
-      float sc[GT];
-  #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float a = 0.f;
-  #pragma unroll
-        for (int e = 0; e < EPL / 2; ++e) a = dot2bf(kw[e], qv[g][e], a);
-        a += dpp_f<0xB1>(a);   // quad_perm [1,0,3,2]
-        a += dpp_f<0x4E>(a);   // quad_perm [2,3,0,1]
-        a += dpp_f<0x141>(a);  // row_half_mirror: joins the two quads of the 8 lanes
-        sc[g] = valid ? a * c : -INFINITY;
-      }
-      // ---- running max over the wave's keys (lazy rescale) ----
-      float mx[GT];
-      bool grow = false;
-  #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float t = fmaxf(sc[g], dpp_f<0x128>(sc[g]));  // row_ror:8 -> other key of the 16-lane row
-        {
-        // v_permlane16_swap: one result holds the even 16-lane row's value and
-        // the other the odd row's, in every lane of the pair of rows
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-        t = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-      }
-        mx[g] = max_halves(t);
-        grow = grow || (mx[g] > m_run[g] + kTauB);
-      }
-      if (__any(grow)) {
-  #pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          const float mn = fmaxf(m_run[g], mx[g]);
-          const float alpha = (mn == -INFINITY) ? 1.0f : fast_exp2(m_run[g] - mn);
-          l_part[g] *= alpha;
-  #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) oacc[g][cb] *= alpha;
-          m_run[g] = mn;
-        }
-      }
-  #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        const float negm = (m_run[g] == -INFINITY) ? 0.f : -m_run[g];
-        const float p = fast_exp2(sc[g] + negm);
-        if (j == 0) {
-          l_part[g] += p;
-          p_lds[wave][g][kk] = (uint16_t)(pack_bf16x2(p, 0.f) & 0xffffu);
-        }
-      }
-      wave_sync();  // p_lds written by the lanes j == 0, read by every lane
-      // ---- values: each lane owns columns 64cb + lane ----
-  #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        const u32x4 pp = *reinterpret_cast<const u32x4*>(&p_lds[wave][g][0]);
-  #pragma unroll
-        for (int kq = 0; kq < 2; ++kq)
-  #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const u32x2 vq = dec_read_tr(vl + vofs[cb] + (32 * pass + 4 * kq) * D * 2);
-            oacc[g][cb] = dot2bf(vq[0], pp[2 * kq], oacc[g][cb]);
-            oacc[g][cb] = dot2bf(vq[1], pp[2 * kq + 1], oacc[g][cb]);
-          }
-      }
-      wave_sync();  // every lane has read p_lds before the next pass rewrites it
-    }
-    if (st + 1 < nst) wait_stage(st + 1);
-    dec_barrier();
-  }
-
-  // ---- merge the four waves' (m, l, o); the ring is idle now (every DMA was
-  // waited for and every wave passed the last barrier), so it holds o ----
-  float(&o_w)[4][GT][D] = *reinterpret_cast<float(*)[4][GT][D]>(&ring[0][0][0]);
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    float s = l_part[g];
-    s += __shfl_xor(s, 8, 64);
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);  // lanes j == 0 held the per-key sums
-    if (lane == 0) {
-      m_w[wave][g] = m_run[g];
-      l_w[wave][g] = s;
-    }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o_w[wave][g][64 * cb + lane] = oacc[g][cb];
-  }
-  __syncthreads();
-  for (int i = tid; i < GT * D; i += 256) {
-    const int g = i / D, d = i % D;
-    float M = m_w[0][g];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, m_w[w][g]);
-    float l = 0.f, a = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(m_w[w][g] - M);  // 0 for a wave that saw no key
-      l = fmaf(l_w[w][g], f, l);
-      a = fmaf(o_w[w][g][d], f, a);
-    }
-    const size_t pidx = ((size_t)b * Hq + h0 + g) * nsplit + split;
-    part_o[pidx * D + d] = a / l;
-    if (d == 0) part_lse[pidx] = M * kLn2 + __logf(l);
-  }
-}
-
-
 // ---------------------------------------------------------------------------
-// bf16 split kernel for GQA groups of 8 or more query heads: matrix cores.
-// The per-key work grows with the heads a workgroup serves; on the VALU (dot2)
-// it saturates from 8 heads on (4.9 TB/s at 8, 2.6 TB/s at 16).  Here
-// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with the
-// GM heads as the 32 columns (unused columns hold zero queries; the matrix
-// cores have ample headroom at HBM speed).  Each wave streams its own 32-key
-// tiles (tiles w, w+4, ... of the chunk) through a private two-slot LDS ring,
-// so no barrier runs per tile; the four waves' (m, l, o) are merged once per
-// chunk.  The register and LDS layouts are those of the prefill kernel: K rows
-// read with ds_read_b128 from 16-byte chunks XOR-swizzled by row, V read
-// transposed with ds_read_b64_tr_b16, P packed from the accumulator into the B
-// operand, a lazily rescaled running max per head.
+// bf16 split kernel: matrix cores.  S^T = K Q^T and O^T += V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 with the query heads of one GQA group (up to 32)
+// as the columns; unused columns hold zero queries.  The products cost the
+// same per key whatever the number of heads, so every K/V byte is read once
+// for the whole group and the matrix cores stay far below their rate at HBM
+// speed.  (A VALU kernel with v_dot2_f32_bf16 grew with the heads served and
+// saturated from 8 heads on.)  Each wave streams its own 32-key tiles (tiles
+// w, w+4, ... of the chunk) through a private two-slot LDS ring, so no
+// barrier runs per tile; the four waves' (m, l, o) are merged once per chunk.
+// The register and LDS layouts are those of the prefill kernel: K rows read
+// with ds_read_b128 from 16-byte chunks XOR-swizzled by row, V read transposed
+// with ds_read_b64_tr_b16, P packed from the accumulator into the B operand, a
+// lazily rescaled running max per head.
 template <int D>
 __device__ __forceinline__ int mk_swz(int row) {  // K: 16 rows x one chunk per read
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -777,18 +460,19 @@ __device__ __forceinline__ int mv_swz(int row) {  // V: 4 rows x 4 chunks per tr
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-template <int D, int GM, bool PAGED>
+// gm (1..32) query heads of one GQA group per workgroup: columns 0..gm-1.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg) {
+    int Hq, int Hkv, int maxlen, int nsplit, int chunk, float c, uint32_t qflip, PagedKV pg, int gm) {
+  constexpr int GM = 32;            // columns (heads) per workgroup, gm of them live
   constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int MD = D / 32;        // 32-row blocks of O^T
   constexpr int RC = D / 8;         // 16-byte chunks per cache row
   constexpr int TILE = 32 * D * 2;  // bytes per 32-key K (or V) tile
   constexpr int RPI = 64 / RC;      // rows per copy instruction (a wave moves 1 KB)
   constexpr int NCP = 32 / RPI;     // copy instructions per K (or V) tile
-  static_assert(GM == 8 || GM == 16 || GM == 32, "heads per workgroup");
   // [wave][slot][K, V]; after the key loop it holds the waves' outputs
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4][2][2][TILE];
   __shared__ float m_w[4][GM], l_w[4][GM];
@@ -803,9 +487,9 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int split = split_of_block(nsplit);
   const int G = Hq / Hkv;
-  const int slices = G / GM;
+  const int slices = G / gm;
   const int kvh = blockIdx.y / slices;
-  const int h0 = kvh * G + (blockIdx.y % slices) * GM;
+  const int h0 = kvh * G + (blockIdx.y % slices) * gm;
   const int b = blockIdx.z;
 
   const int L = min(max(seqlens[b], 0), maxlen);
@@ -826,16 +510,16 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
     __syncthreads();
   }
 
-  // Q^T fragments (B operand): column x = head h0 + x (zero past GM),
+  // Q^T fragments (B operand): column x = head h0 + x (zero past gm),
   // d = 16ks + 8hi + 0..7.  Used at once, so their loads are waited for here
   // and not inside the key loop (where the counter also sees the copies).
   bf16x8 qf[KS];
   {
-    const uint16_t* qr = q + ((size_t)b * Hq + h0 + min(x, GM - 1)) * D + hi * 8;
+    const uint16_t* qr = q + ((size_t)b * Hq + h0 + min(x, gm - 1)) * D + hi * 8;
     u32x4 w[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u32x4*>(qr + ks * 16);
-    const uint32_t keep = x < GM ? 0xffffffffu : 0u;
+    const uint32_t keep = x < gm ? 0xffffffffu : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (w[ks] ^ qflip) & keep);
   }
@@ -952,7 +636,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
   const float lt = sum_halves(l_run);
   __syncthreads();  // every copy landed and every read finished: the ring is free
   float(&o_w)[4][GM][D] = *reinterpret_cast<float(*)[4][GM][D]>(&ring[0][0][0][0]);
-  if (x < GM) {
+  if (x < gm) {
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -963,7 +647,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
     }
   }
   __syncthreads();
-  for (int i = tid; i < GM * D; i += 256) {
+  for (int i = tid; i < gm * D; i += 256) {
     const int g = i / D, d = i % D;
     float M = m_w[0][g];
 #pragma unroll
@@ -981,21 +665,22 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
   }
 }
 
-// Query heads per bf16 split workgroup for a GQA group of G heads: groups of
-// 8 or more (multiples of 8) run on the matrix-core kernel with up to 32 heads
-// per workgroup; smaller ones on the VALU kernel with 4, 2 or 1.
-bool bf16_uses_mfma(int G) { return G % 8 == 0; }
+// Query heads per bf16 split workgroup for a GQA group of G heads: the whole
+// group up to 32 (every K/V byte is then read once), else the largest divisor
+// of G that fits the 32 matrix columns.
 int bf16_group_tile(int G) {
-  if (bf16_uses_mfma(G)) return G % 32 == 0 ? 32 : G % 16 == 0 ? 16 : 8;
-  return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  if (G <= 32) return G;
+  for (int t = 32; t > 1; --t)
+    if (G % t == 0) return t;
+  return 1;
 }
 
 // Keys per bf16 split workgroup: the largest of 2048, 1024, 512, 256 that
-// still gives at least two full rounds of resident workgroups (4 per CU on
-// 256 CUs) when every sequence is maxlen long; long chunks amortise the
-// per-chunk prologue and partials, short ones keep small batches parallel.
-// (GQA B64 workload, non-temporal copies: 2048 keys 6.15 TB/s, 1024 6.03,
-// 3072 6.14, 4096 6.02, 512 5.83.)
+// still gives at least 2048 workgroups when every sequence is maxlen long;
+// long chunks amortise the per-chunk prologue and partials, short ones keep
+// small batches parallel.  (Measured on the GQA B64 workload with the earlier
+// VALU kernel: 2048 keys 6.15 TB/s, 1024 6.03, 3072 6.14, 4096 6.02, 512
+// 5.83.)
 int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   const long long rows = (long long)B * Hkv * ((Hq / Hkv) / bf16_group_tile(Hq / Hkv));
   static_assert(kMaxChunkB == 2048, "the longest chunk sizes the page-id table");
@@ -1005,30 +690,9 @@ int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   return 256;
 }
 
-template <int D, int GT, bool PAGED>
-hipError_t launch_bf16(const DecodeArgs& a, hipStream_t stream) {
-  const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
-  if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
-  const int nsplit = (a.maxlen + chunk - 1) / chunk;
-  const int G = a.Hq / a.Hkv;
-  float* part_o = static_cast<float*>(a.ws);
-  const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
-  dim3 g1(nsplit, a.Hkv * (G / GT), a.B);
-  if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_bf16_split_kernel<D, GT, PAGED>), g1, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
-                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u, a.paged);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
-                     part_lse, a.seqlens, static_cast<uint16_t*>(a.o), a.Hq, a.maxlen, nsplit, chunk);
-  return hipGetLastError();
-}
-
-template <int D, int GM, bool PAGED>
+template <int D, bool PAGED>
 hipError_t launch_bf16_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const int gm = bf16_group_tile(a.Hq / a.Hkv);
   const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
   if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
   const int nsplit = (a.maxlen + chunk - 1) / chunk;
@@ -1036,12 +700,12 @@ hipError_t launch_bf16_mfma(const DecodeArgs& a, hipStream_t stream) {
   float* part_o = static_cast<float*>(a.ws);
   const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
-  dim3 g1(nsplit, a.Hkv * (G / GM), a.B);
+  dim3 g1(nsplit, a.Hkv * (G / gm), a.B);
   if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_bf16_mfma_kernel<D, GM, PAGED>), g1, dim3(256), 0, stream,
+  hipLaunchKernelGGL((decode_bf16_mfma_kernel<D, PAGED>), g1, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.seqlens, part_o, part_lse, a.Hq, a.Hkv, a.maxlen,
-                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u, a.paged);
+                     nsplit, chunk, a.c, a.neg ? 0x80008000u : 0u, a.paged, gm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D>), dim3(a.Hq, a.B), dim3(kCombThreads), 0, stream, part_o,
@@ -1051,14 +715,7 @@ hipError_t launch_bf16_mfma(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, bool PAGED>
 hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
-  switch (bf16_group_tile(a.Hq / a.Hkv)) {
-    case 32: return launch_bf16_mfma<D, 32, PAGED>(a, stream);
-    case 16: return launch_bf16_mfma<D, 16, PAGED>(a, stream);
-    case 8: return launch_bf16_mfma<D, 8, PAGED>(a, stream);
-    case 4: return launch_bf16<D, 4, PAGED>(a, stream);
-    case 2: return launch_bf16<D, 2, PAGED>(a, stream);
-    default: return launch_bf16<D, 1, PAGED>(a, stream);
-  }
+  return launch_bf16_mfma<D, PAGED>(a, stream);
 }
 
 template <typename T, int D, int GT>

@@ -15,8 +15,9 @@
 //     memory requirements for inference in large language models", GQA
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
-//     bf16 path (chunks of 2048, 1024, 512 or 256 keys, the largest that
-//       still gives 2048 workgroups): one workgroup serves the whole GQA group
+//     bf16 path (chunks of 4096, 2048, 1024, 512 or 256 keys, the largest
+//       that still gives 2048 workgroups): one workgroup serves the whole GQA
+//       group
 //       (up to 32 query heads).  Each of its four waves streams its own
 //       32-key tiles of the chunk through a private two-slot LDS ring, copied
 //       HBM -> LDS by global_load_lds_dwordx4 (no VGPR staging, no per-tile
@@ -430,7 +431,7 @@ __device__ __forceinline__ void dec_dma16_addr(const void* addr, uint8_t* lds_wa
 // Longest bf16 chunk (keys), and the most pool pages one chunk touches: its
 // keys over pages of >= 16 keys, plus one page for a chunk that does not start
 // on a page boundary.
-constexpr int kMaxChunkB = 2048;
+constexpr int kMaxChunkB = 4096;
 constexpr int kMaxChunkPages = kMaxChunkB / 16 + 1;
 typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 dec_read_tr(const uint8_t* p) {
@@ -505,8 +506,8 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void decode_bf16_mfma_kernel
   const int slot0 = PAGED ? (kbeg >> pg.page_shift) : 0;
   if (PAGED) {
     const int nslots = ((kbeg + n - 1) >> pg.page_shift) - slot0 + 1;  // <= kMaxChunkPages
-    if (tid < nslots)
-      pid_lds[tid] = min(max(pg.block_table[(size_t)b * pg.max_pages + slot0 + tid], 0), pg.num_pages - 1);
+    for (int i = tid; i < nslots; i += 256)
+      pid_lds[i] = min(max(pg.block_table[(size_t)b * pg.max_pages + slot0 + i], 0), pg.num_pages - 1);
     __syncthreads();
   }
 
@@ -675,16 +676,16 @@ int bf16_group_tile(int G) {
   return 1;
 }
 
-// Keys per bf16 split workgroup: the largest of 2048, 1024, 512, 256 that
-// still gives at least 2048 workgroups when every sequence is maxlen long;
-// long chunks amortise the per-chunk prologue and partials, short ones keep
-// small batches parallel.  (Measured on the GQA B64 workload with the earlier
-// VALU kernel: 2048 keys 6.15 TB/s, 1024 6.03, 3072 6.14, 4096 6.02, 512
-// 5.83.)
+// Keys per bf16 split workgroup: the largest of 4096, 2048, 1024, 512, 256
+// that still gives at least 2048 workgroups when every sequence is maxlen
+// long; long chunks amortise the per-chunk prologue and partials, short ones
+// keep small batches parallel.  (GQA B64 Hkv8 workload, lengths 1K-32K, 4 and
+// 8 heads per group: 4096 keys 6.66 / 6.41 TB/s, 2048 6.48 / 6.17, 1024
+// 5.50 / 5.02, 8192 5.08 / 5.02.)
 int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   const long long rows = (long long)B * Hkv * ((Hq / Hkv) / bf16_group_tile(Hq / Hkv));
-  static_assert(kMaxChunkB == 2048, "the longest chunk sizes the page-id table");
-  for (int chunk : {2048, 1024, 512}) {
+  static_assert(kMaxChunkB == 4096, "the longest chunk sizes the page-id table");
+  for (int chunk : {4096, 2048, 1024, 512}) {
     if (rows * ((maxlen + chunk - 1) / chunk) >= 2048) return chunk;
   }
   return 256;

@@ -201,6 +201,19 @@ def test_decode_long_chunk_boundaries():
     assert torch.all(o[0] == 0)
 
 
+def test_decode_4096_key_chunk_boundaries():
+    """B32 Hq32 Hkv8 d128 with a 32768-key cache launches 4096-key chunks:
+    lengths on and around their boundaries (and the 32-key tiles inside
+    them), empty and single-key rows."""
+    lens = [0, 1, 31, 32, 33, 4095, 4096, 4097, 8191, 8192, 8193, 12288, 16383, 16385, 20000, 24575,
+            24576, 24577, 28000, 32767, 32768, 2, 100, 4000, 4127, 7000, 9000, 15000, 30000, 31000, 5, 12345]
+    q, kc, vc, ls, scale = I.decode_inputs(len(lens), 32, 8, 128, 1, 32768, 32768, "bf16", seed=10, seqlens=lens)
+    o = gpu_decode(q, kc, vc, ls, scale)
+    ro, _ = oracle.decode(q, kc, vc, ls, scale)
+    check_bf16(o, ro, "decode 4096-key chunks")
+    assert torch.all(o[0] == 0)
+
+
 def test_decode_matches_last_prefill_row():
     """Decode of token i against K,V[0..i] equals causal prefill row i (both on the GPU)."""
     q, k, v, scale = I.prefill_inputs(2, 8, 2, 700, 128, "bf16", seed=23)

@@ -506,7 +506,7 @@ def main():
         result["decode"] = {"workload": dc.name, "ms_avg": d_avg, "ms_median": d_ms[K // 2],
                             "ms_min": d_ms[0], "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
                             "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (d_avg * 1e-3),
-                            "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel",
+                            "roofline": {"kernel": "decode_bf16_mfma_kernel + decode_combine_kernel",
                                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
@@ -532,7 +532,7 @@ def main():
                                   "ms_avg": g_avg, "ms_median": g_ms[K // 2], "ms_min": g_ms[0],
                                   "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
                                   "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (g_avg * 1e-3),
-                                  "roofline": {"kernel": "decode_bf16_split_kernel<paged> + decode_combine_kernel",
+                                  "roofline": {"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
                                                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
         if result["value"] is None:

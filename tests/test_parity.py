@@ -214,6 +214,23 @@ def test_decode_4096_key_chunk_boundaries():
     assert torch.all(o[0] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 3.0])
+def test_decode_scale_sign_zero_and_large(dtype, G, scale):
+    """Negative scale (query signs flipped, positive exponent coefficient),
+    zero scale (uniform weights over the visible keys) and scores near 1e2
+    (no overflow), for both decode paths."""
+    lens = [1, 31, 33, 300, 1024, 1300, 5]
+    q, kc, vc, ls, _ = I.decode_inputs(len(lens), 2 * G, 2, 128, 1, 1300, 1300, dtype, seed=70 + G, seqlens=lens)
+    o = gpu_decode(q, kc, vc, ls, scale)
+    ro, _ = oracle.decode(q, kc, vc, ls, scale)
+    if dtype == "f32":
+        check_close(o, ro, F32_MAX_ABS, "decode f32 scale")
+    else:
+        check_bf16(o, ro, "decode bf16 scale")
+
+
 def test_decode_matches_last_prefill_row():
     """Decode of token i against K,V[0..i] equals causal prefill row i (both on the GPU)."""
     q, k, v, scale = I.prefill_inputs(2, 8, 2, 700, 128, "bf16", seed=23)

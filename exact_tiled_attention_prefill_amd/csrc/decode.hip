@@ -16,7 +16,7 @@
 //     paragraph).  Output per chunk: its normalised partial o_s and its
 //     log-sum-exp.
 //     bf16 path (chunks of 4096, 2048, 1024, 512 or 256 keys, the largest
-//       that still gives 2048 workgroups): one workgroup serves the whole GQA
+//       that still gives 1024 workgroups): one workgroup serves the whole GQA
 //       group
 //       (up to 32 query heads).  Each of its four waves streams its own
 //       32-key tiles of the chunk through a private two-slot LDS ring, copied
@@ -677,16 +677,18 @@ int bf16_group_tile(int G) {
 }
 
 // Keys per bf16 split workgroup: the largest of 4096, 2048, 1024, 512, 256
-// that still gives at least 2048 workgroups when every sequence is maxlen
-// long; long chunks amortise the per-chunk prologue and partials, short ones
-// keep small batches parallel.  (GQA B64 Hkv8 workload, lengths 1K-32K, 4 and
-// 8 heads per group: 4096 keys 6.66 / 6.41 TB/s, 2048 6.48 / 6.17, 1024
-// 5.50 / 5.02, 8192 5.08 / 5.02.)
+// that still gives at least 1024 workgroups (four rounds of one workgroup per
+// CU) when every sequence is maxlen long; long chunks amortise the per-chunk
+// prologue and partials, short ones keep small batches parallel.  (GQA B64
+// Hkv8 workload, lengths 1K-32K, 4 and 8 heads per group: 4096 keys 6.66 /
+// 6.41 TB/s, 2048 6.48 / 6.17, 1024 5.50 / 5.02, 8192 5.08 / 5.02.  Asking
+// for 1024 rather than 2048 workgroups doubles the chunk for small batches
+// and short caches: +2-3% there; asking for 4096 loses 6-10%.)
 int bf16_decode_chunk(int B, int Hq, int Hkv, int maxlen) {
   const long long rows = (long long)B * Hkv * ((Hq / Hkv) / bf16_group_tile(Hq / Hkv));
   static_assert(kMaxChunkB == 4096, "the longest chunk sizes the page-id table");
   for (int chunk : {4096, 2048, 1024, 512}) {
-    if (rows * ((maxlen + chunk - 1) / chunk) >= 2048) return chunk;
+    if (rows * ((maxlen + chunk - 1) / chunk) >= 1024) return chunk;
   }
   return 256;
 }

@@ -191,10 +191,10 @@ def test_decode_lengths_and_groups(dtype, d, G):
 
 
 def test_decode_long_chunk_boundaries():
-    """B16 Hq32 Hkv8 d128 with a 32768-key cache launches 2048-key chunks:
+    """B16 Hq32 Hkv4 d128 with a 32768-key cache launches 2048-key chunks:
     lengths on and around their boundaries, and empty / single-key rows."""
     lens = [0, 1, 2047, 2048, 2049, 4095, 4096, 4097, 30000, 32767, 32768, 6144, 100, 2, 8191, 16385]
-    q, kc, vc, ls, scale = I.decode_inputs(len(lens), 32, 8, 128, 1, 32768, 32768, "bf16", seed=9, seqlens=lens)
+    q, kc, vc, ls, scale = I.decode_inputs(len(lens), 32, 4, 128, 1, 32768, 32768, "bf16", seed=9, seqlens=lens)
     o = gpu_decode(q, kc, vc, ls, scale)
     ro, _ = oracle.decode(q, kc, vc, ls, scale)
     check_bf16(o, ro, "decode 2048-key chunks")

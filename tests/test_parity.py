@@ -176,7 +176,7 @@ def test_decode_gqa_workload():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 37, 48, 64])
 def test_decode_lengths_and_groups(dtype, d, G):
     lens = [0, 1, 2, 511, 512, 513, 1024, 1100, 1300, 7]
     q, kc, vc, ls, scale = I.decode_inputs(len(lens), 2 * G, 2, d, 1, 1300, 1300, dtype, seed=G + d,

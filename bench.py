@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-One step = one fa_prefill call on the causal MHA workload (B4 H32 N4096
-d128 bf16), one fa_decode call on the GQA decode workload (B64 Hq32 Hkv8 d128
-bf16, cache lengths uniform in [1024, 32768]), one fa_decode_paged call on
-the same logical caches in 64-key pages of a shuffled pool, and two
-fa_prefill_varlen calls: a 4096-query chunk against a 16384-key prefix (GQA B2
-Hq32 Hkv8 d128, causal) and the MHA 4K workload with a 1024-key causal window.
-Inputs are seeded synthetic tensors already resident in HBM before timing
-starts.
+One step = one fa_prefill call on the long-context causal GQA workload
+(B1 Hq64 Hkv8 N131072 d128 bf16) followed by one fa_decode call on the GQA
+decode workload (B64 Hq32 Hkv8 d128 bf16, cache lengths uniform in
+[1024, 32768]): the prefill covers the tiled score / mask / running-softmax /
+value steps, the decode the split-KV read of a cache and its log-sum-exp
+combine.  `value` is the prefill's TFLOP/s (algorithmic FLOPs =
+4*d*B*Hq*N(N+1)/2 over the prefill kernel's own HIP-event time).
 
-`value` is prefill TFLOP/s (algorithmic FLOPs = 4*d*B*Hq*(N(N+1)/2) over the
-prefill kernel's own HIP-event time); the decode figures (KV bytes read per
-second) are reported beside it.  Kernel durations come from HIP events
-recorded on the stream the kernels are launched on.  A bounded sample of the
-fp64 CPU oracle is timed on the host as a reported baseline, and the
-device's sustained MFMA and HBM-read rates are measured after the timed
-region.
+After the timed steps, the other workloads are timed as legs with their own
+step counts: causal MHA B4 H32 N4096, causal GQA B2 Hq32 Hkv8 N16384, decode
+against the same caches in 64-key pages of a shuffled pool, a packed
+4096-query chunk against a 16384-key prefix, the MHA 4K workload with a
+1024-key window, and the MHA 4K backward.  Inputs are seeded synthetic
+tensors already resident in HBM before timing starts; kernel durations come
+from HIP events recorded on the stream the kernels are launched on.
+
+The fp64 CPU oracle runs on the host in a pool of worker processes (started
+before anything touches the GPU): on sampled rows of every head of the 128K
+workload (timed: that is `cpu_baseline`), on every row of the 16K and 4K
+workloads; each compares its rows with the GPU's output of the timed runs
+(`parity`).  The device's sustained MFMA and HBM-read rates are measured
+after the timed region.
 
 Prints ONE JSON line.  --gpus N with N > 1 exits: the kernels run on one GPU.
 """
@@ -36,8 +42,12 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-PREFILL_SRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc", "prefill_bf16.hip")
-DECODE_SRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc")
+PREFILL_SRC = os.path.join(CSRC, "prefill_bf16.hip")
+DECODE_SRC = os.path.join(CSRC, "decode.hip")
+BACKWARD_SRC = os.path.join(CSRC, "backward_bf16.hip")
+BAR = {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3}
+PREFILL_KERNEL = "prefill_bf16_kernel<128, causal> (4 or 8 waves per workgroup, as the launcher picks)"
 
 
 def prefill_flops(B, Hq, N, d, causal):
@@ -57,16 +67,6 @@ def varlen_pairs(lens, causal, window):
     return total
 
 
-def prefill_waves(d, causal, n_q, n_k, window=-1):
-    """Waves per prefill workgroup that the library's launcher picks (for
-    the kernel labels): 8 when the average query row of sequences with n_q
-    queries against n_k keys sees 8192 keys or more at d = 128, else 4."""
-    keys = n_k - ((n_q - 1) / 2 if causal else 0)
-    if window >= 0:
-        keys = min(keys, window + 1)
-    return 8 if d == 128 and keys >= 8192 else 4
-
-
 def prefill_bytes(B, Hq, Hkv, N, d, elem=2):
     return (2 * B * Hq * N * d + 2 * B * Hkv * N * d) * elem + B * Hq * N * 4
 
@@ -80,34 +80,36 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(name, src):
-    """HBM bytes per launch from a committed rocprofv3 counter summary.
-
-    profiles/<name>.md carries a line `traffic_bytes_per_launch: <int>` and
-    `kernel_source_sha: <hash>`; the figure is only used while the kernel
-    source still has that hash (otherwise null: the counters are stale).
-    """
-    path = os.path.join(PROFILES, name + ".md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    h = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
-    if not m or not h or h.group(1) != source_hash(src):
-        return None
-    return float(m.group(1))
-
-
-def measured_counters(name, src, keys):
-    """Derived rocprofv3 counter figures (MFMA busy fraction, counted MFMA
-    FLOPs over algorithmic FLOPs, clock, HBM rate) from a committed summary,
-    used only while the kernel source still has the summary's hash."""
+def _summary(name, src):
+    """Text of profiles/<name>.md if its kernel_source_sha matches `src`."""
     path = os.path.join(PROFILES, name + ".md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     if not h or h.group(1) != source_hash(src):
+        return None
+    return text
+
+
+def measured_traffic(name, src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary.
+
+    profiles/<name>.md carries `traffic_bytes_per_launch: <number>` and
+    `kernel_source_sha: <hash>`; the figure is used only while the kernel
+    source still has that hash (otherwise null: the counters are stale).
+    """
+    text = _summary(name, src)
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text) if text else None
+    return float(m.group(1)) if m else None
+
+
+def measured_counters(name, src, keys):
+    """Derived rocprofv3 counter figures (MFMA busy fraction, counted MFMA
+    FLOPs over algorithmic FLOPs, clock, HBM rate) from a committed summary,
+    used only while the kernel source still has the summary's hash."""
+    text = _summary(name, src)
+    if text is None:
         return None
     out = {}
     for key in keys:
@@ -120,10 +122,10 @@ def measured_counters(name, src, keys):
 def measured_ceilings():
     """Sustained MFMA and HBM-read rates of this device from libfa_probes.so.
 
-    The nominal peaks above assume the 2.4 GHz boost clock; under dense MFMA
-    load on random operands the part is power-limited, so the rate the matrix
-    cores actually sustain (and HBM's practical read rate) is measured here
-    and reported beside them.  Returns None if the probe library is absent.
+    Context only: the roofline fractions are against the published peaks.
+    Under dense MFMA load on random operands the part is power-limited, so the
+    matrix cores sustain less than the nominal rate; HBM's practical read rate
+    is likewise below 8 TB/s.  Returns None if the probe library is absent.
     """
     import ctypes
 
@@ -151,9 +153,9 @@ def measured_ceilings():
         reads[name] = gbs.value
     out["hbm_read_gbs"] = max(reads.values())
     out["hbm_read_gbs_by_hint"] = reads
-    out["note"] = ("whole-chip sustained v_mfma_f32_32x32x16_bf16 rate (two waves per SIMD, operands in "
-                   "registers) and a 4 GiB read-only stream with 16-byte loads, with and without the "
-                   "non-temporal hint (hbm_read_gbs is the faster)")
+    out["note"] = ("context only, not a roofline: whole-chip sustained v_mfma_f32_32x32x16_bf16 rate (two "
+                   "waves per SIMD, operands in registers) and a 4 GiB read-only stream with 16-byte loads, "
+                   "with and without the non-temporal hint (hbm_read_gbs is the faster)")
     return out
 
 
@@ -170,106 +172,127 @@ def device_memory(fn, io, workspace, n_by_n):
     fn()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
-    return {"io_bytes": sum(t.numel() * t.element_size() for t in io), "workspace_bytes": workspace,
-            "allocated_before_call": before, "peak_during_call": peak,
-            "extra_over_call": peak - before, "n_by_n_fp32_scores_bytes": n_by_n}
+    io_bytes = sum(t.numel() * t.element_size() for t in io)
+    return {"io_bytes": io_bytes, "workspace_bytes": workspace, "allocated_before_call": before,
+            "peak_during_call": peak, "extra_over_call": peak - before, "n_by_n_fp32_scores_bytes": n_by_n,
+            "call_allocates_nothing": peak == before}
 
 
+# ---------------------------------------------------------------- oracle pool
 def _oracle_pool_init():
     """Process-pool worker start-up: one BLAS thread per worker process."""
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
         os.environ[var] = "1"
 
 
-def _oracle_head(job):
-    """One (batch, head) of the causal prefill workload through the fp64 oracle
-    (run in a pool worker): every query row, and the GPU output's error on
-    them.  Tensors arrive as raw bf16 bits (uint16) and lse as float32."""
+def _oracle_job(job):
+    """Causal prefill rows of one KV group's query heads through the fp64
+    oracle (run in a pool worker), and the GPU output's error on them.
+    Tensors arrive as raw bf16 bits (uint16), lse as float32; q holds only the
+    requested rows of each head."""
     import numpy as np
 
     import oracle
 
-    qh, kh, vh, oh, lh, scale = job
+    n, rows, q_rows, kh, vh, o_rows, l_rows, scale = job
     bf16 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)  # exact bf16 -> fp32
-    n, d = qh.shape
-    q4, k4, v4 = (bf16(a)[None, None] for a in (qh, kh, vh))
-    ro, rl = oracle.attention_rows(q4, k4, v4, True, scale, np.arange(n), [(0, 0)])
-    e = np.abs(bf16(oh).astype(np.float64) - ro[0])
-    el = np.abs(lh.astype(np.float64) - rl[0])
-    return 4 * d * n * (n + 1) // 2, float(e.max()), float(e.sum()), int(e.size), float(el.max())
+    d = kh.shape[1]
+    k4, v4 = bf16(kh)[None, None], bf16(vh)[None, None]
+    flops, emax, esum, count, lmax = 0, 0.0, 0.0, 0, 0.0
+    q4 = np.zeros((1, 1, n, d), dtype=np.float32)
+    for qh, oh, lh in zip(q_rows, o_rows, l_rows):
+        q4[0, 0, rows] = bf16(qh)
+        ro, rl = oracle.attention_rows(q4, k4, v4, True, scale, rows, [(0, 0)])
+        e = np.abs(bf16(oh).astype(np.float64) - ro[0])
+        el = np.abs(lh.astype(np.float64) - rl[0])
+        flops += int(sum(4 * d * (int(r) + 1) for r in rows))
+        emax, esum, count, lmax = max(emax, float(e.max())), esum + float(e.sum()), count + e.size, max(
+            lmax, float(el.max()))
+    return flops, emax, esum, count, lmax
 
 
-def cpu_baseline_pool(pool, workers, q, k, v, scale, o_gpu, lse_gpu):
-    """Time the fp64 oracle on the WHOLE prefill workload (every causal row of
-    every (batch, head)), spread over a pool of worker processes, and report
-    the GPU output's error on all of it."""
+def oracle_check(pool, q, k, v, scale, o_gpu, lse_gpu, rows, heads_per_job):
+    """Compare the GPU output at `rows` of every (batch, head) with the oracle,
+    jobs of `heads_per_job` query heads of one KV group.  Returns the error
+    summary, the algorithmic FLOPs evaluated and the wall time."""
+    import numpy as np
     import torch
 
     B, Hq, N, d = q.shape
     G = Hq // k.shape[1]
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = torch.as_tensor(rows)
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view("uint16")
-    jobs = ((bits(q[b, h]), bits(k[b, h // G]), bits(v[b, h // G]), bits(o_gpu[b, h]),
-             lse_gpu[b, h].contiguous().numpy(), scale) for b in range(B) for h in range(Hq))
+
+    def jobs():
+        for b in range(B):
+            for h0 in range(0, Hq, heads_per_job):
+                hs = range(h0, min(h0 + heads_per_job, Hq))
+                g = h0 // G
+                assert all(h // G == g for h in hs)
+                yield (N, rows, [bits(q[b, h][idx]) for h in hs], bits(k[b, g]), bits(v[b, g]),
+                       [bits(o_gpu[b, h][idx]) for h in hs], [lse_gpu[b, h][idx].numpy() for h in hs], scale)
+
     t0 = time.perf_counter()
-    res = list(pool.imap_unordered(_oracle_head, jobs, chunksize=1))
+    res = list(pool.imap_unordered(_oracle_job, jobs(), chunksize=1))
     dt = time.perf_counter() - t0
-    flops = sum(r[0] for r in res)
     count = sum(r[3] for r in res)
-    o_max, o_mean, l_max = max(r[1] for r in res), sum(r[2] for r in res) / count, max(r[4] for r in res)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
-            "sample": f"the whole B{B} H{Hq} N{N} d{d} causal workload ({B * Hq} heads x {N} rows), fp64 numpy, "
-                      f"{workers} worker processes with 1 BLAS thread each, {dt:.1f} s wall (inputs pickled "
-                      f"to the workers inside the timed span); the rate is algorithmic FLOPs over wall time",
-            "gpu_error_on_these_rows": {
-                "rows": "all", "o_max_abs": o_max, "o_mean_abs": o_mean, "lse_max_abs": l_max,
-                "bar": {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3},
-                "within_bar": o_max <= 2e-2 and o_mean <= 2e-3 and l_max <= 1e-3}}
+    err = {"o_max_abs": max(r[1] for r in res), "o_mean_abs": sum(r[2] for r in res) / count,
+           "lse_max_abs": max(r[4] for r in res)}
+    err["within_bar"] = all(err[key] <= BAR[key] for key in BAR)
+    return err, sum(r[0] for r in res), dt
 
 
-def cpu_baseline(q, k, v, scale, seconds, o_gpu=None, lse_gpu=None):
-    """Time the fp64 oracle on sampled causal rows of the prefill workload.
+def c5_sample_rows(n, count=2048, seed=3):
+    """Rows of the 128K workload the oracle evaluates on every head: the
+    first and last rows, multiples of 64 +- 1 in the first 1024 rows, rows
+    next to powers of two, and seeded uniform rows up to `count`."""
+    import torch
 
-    When the GPU's output (host copies) is given, the same oracle rows also
-    give the error of those rows: max-abs / mean-abs of O and max-abs of lse.
-    """
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+    rows = {0, 1, 2, 3, n - 2, n - 1}
+    for m in range(64, 1025, 64):
+        rows.update((m - 1, m, m + 1))
+    p = 1
+    while p < n:
+        rows.update(r for r in (p - 1, p, p + 1) if 0 <= r < n)
+        p *= 2
+    gen = torch.Generator().manual_seed(seed)
+    for r in torch.randint(0, n, (4 * count,), generator=gen).tolist():
+        if len(rows) >= count:
+            break
+        rows.add(int(r))
+    return sorted(rows)
 
-    import oracle
-    from exact_tiled_attention_prefill_amd.inputs import sample_rows
 
-    B, Hq, N, d = q.shape
-    rows = sample_rows(N, 2048, seed=3)  # ~2100 rows spread over the sequence, per head
-    heads = [(b, h) for b in range(B) for h in range(Hq)]
-    done_flops, done_rows, done_heads, t0 = 0, 0, 0, time.perf_counter()
-    err = {"o_max_abs": 0.0, "o_abs_sum": 0.0, "o_count": 0, "lse_max_abs": 0.0}
-    with threadpool_limits(limits=1):
-        for b, h in heads:
-            ro, rl = oracle.attention_rows(q, k, v, True, scale, rows, [(b, h)])
-            done_flops += sum(4 * d * (r + 1) for r in rows)
-            done_rows += len(rows)
-            done_heads += 1
-            if o_gpu is not None:
-                e = np.abs(o_gpu[b, h, rows].double().numpy() - ro[0])
-                err["o_max_abs"] = max(err["o_max_abs"], float(e.max()))
-                err["o_abs_sum"] += float(e.sum())
-                err["o_count"] += e.size
-                el = np.abs(lse_gpu[b, h, rows].double().numpy() - rl[0])
-                err["lse_max_abs"] = max(err["lse_max_abs"], float(el.max()))
-            if time.perf_counter() - t0 >= seconds:
-                break
-    dt = time.perf_counter() - t0
-    out = {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-           "sample": f"{done_rows} causal query rows ({len(rows)} sampled rows x {done_heads} heads) of "
-                     f"the B4 H32 N4096 d128 workload, fp64 numpy, {dt:.1f} s, 1 BLAS thread; "
-                     f"the rate is algorithmic FLOPs of those rows over wall time"}
-    if o_gpu is not None and err["o_count"]:
-        mean = err["o_abs_sum"] / err["o_count"]
-        out["gpu_error_on_these_rows"] = {
-            "o_max_abs": err["o_max_abs"], "o_mean_abs": mean, "lse_max_abs": err["lse_max_abs"],
-            "bar": {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3},
-            "within_bar": err["o_max_abs"] <= 2e-2 and mean <= 2e-3 and err["lse_max_abs"] <= 1e-3}
-    return out
+# ---------------------------------------------------------------- timing
+def time_calls(fn, stream, steps):
+    """HIP-event times (ms) of `steps` back-to-back calls on `stream`."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def stats(ms):
+    k = len(ms)
+    return {"ms_avg": sum(ms) / k, "ms_median": ms[k // 2], "ms_min": ms[0], "launches": k}
+
+
+def mfma_roofline(kernel, tflops, counters_name=None, src=PREFILL_SRC, algorithmic_bytes=None):
+    rl = {"kernel": kernel, "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+    if algorithmic_bytes is not None:
+        rl["algorithmic_bytes"] = algorithmic_bytes
+    if counters_name is not None:
+        rl["traffic"] = measured_traffic(counters_name, src)
+        rl["rocprof"] = measured_counters(counters_name, src, ("mfma_busy_fraction", "mfma_flops_over_algorithmic",
+                                                               "shader_clock_ghz", "traffic_over_algorithmic"))
+    return rl
 
 
 def main():
@@ -277,37 +300,36 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (cpu_baseline and the parity of the timed outputs)")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
-    ap.add_argument("--no-configs", action="store_true",
-                    help="skip the 16K and 128K causal GQA prefill configurations")
+    ap.add_argument("--no-legs", action="store_true", help="time only the step (128K prefill + decode)")
     ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_paged", "prefill_chunked", "prefill_window",
-                                       "backward", "prefill_gqa_16k", "prefill_gqa_128k", "copy", "ceiling"],
+    ap.add_argument("--only", choices=["step", "prefill_gqa_128k", "decode", "prefill_mha_4k", "prefill_gqa_16k",
+                                       "decode_paged", "prefill_chunked", "prefill_window", "backward", "copy",
+                                       "ceiling"],
                     default=None,
-                    help="run one kernel only (for profiler runs); 'copy' runs a plain 1 GiB device "
-                         "copy used to calibrate the HBM byte counters; 'ceiling' runs only the "
-                         "MFMA / HBM ceiling probes")
+                    help="run one kernel only (for profiler runs); 'step' runs the 128K prefill and the decode; "
+                         "'copy' runs a plain 1 GiB device copy used to calibrate the HBM byte counters; "
+                         "'ceiling' runs only the MFMA / HBM ceiling probes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); nothing to do for N > 1.",
               file=sys.stderr)
         sys.exit(2)
+    only = args.only
+    want = lambda name: only is None or only == name or (only == "step" and name in ("prefill_gqa_128k", "decode"))
+    run_legs = only is not None or not args.no_legs
+    leg = lambda name: want(name) and run_legs
 
     # The oracle's worker processes start before anything touches the GPU (a
     # process that has initialised the GPU does not start new programs).
     pool, workers = None, 0
-    if args.only in (None, "prefill") and not args.no_cpu_baseline:
-        try:
-            import multiprocessing
+    if only is None and not args.no_cpu_baseline:
+        import multiprocessing
 
-            workers = max(1, min(16, len(os.sched_getaffinity(0))))
-            pool = multiprocessing.get_context("spawn").Pool(workers, initializer=_oracle_pool_init)
-        except Exception as exc:  # fall back to the single-thread sampled baseline
-            print(f"oracle process pool unavailable ({exc}); timing a single-thread sample", file=sys.stderr)
-            pool = None
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        pool = multiprocessing.get_context("spawn").Pool(workers, initializer=_oracle_pool_init)
 
     import torch
 
@@ -318,10 +340,10 @@ def main():
 
     load_library()  # fail loudly before any work if libfa.so is missing
     dev = torch.device("cuda:0")
-    if args.only == "ceiling":
+    if only == "ceiling":
         print(json.dumps({"ceilings": measured_ceilings()}), flush=True)
         return
-    if args.only == "copy":
+    if only == "copy":
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(args.warmup + args.steps):
@@ -330,61 +352,155 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": 1 << 30, "launches": args.warmup + args.steps}))
         return
     stream = torch.cuda.current_stream()
-    out = {}
-    run_prefill = args.only in (None, "prefill")
-    run_decode = args.only in (None, "decode") and not args.no_decode
-    run_paged = args.only in (None, "decode_paged") and not args.no_decode
-    run_chunk = args.only in (None, "prefill_chunked")
-    run_window = args.only in (None, "prefill_window")
-    run_bwd = args.only in (None, "backward")
+    K = args.steps
+    result = {
+        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV-read GB/s (% HBM)",
+        "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+    }
+    host = {}  # CPU copies of inputs and GPU outputs for the oracle
 
-    pc = I.PREFILL_MHA_4K
-    if run_prefill:
-        q, k, v, scale = I.prefill_config_inputs(pc)
+    def prefill_setup(cfg):
+        q, k, v, scale = I.prefill_config_inputs(cfg)
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
         od = torch.empty_like(qd)
-        lsed = torch.empty((pc.B, pc.Hq, pc.N), dtype=torch.float32, device=dev)
+        ld = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
 
-        def pf():
-            prefill(qd, kd, vd, causal=True, scale=scale, out=od, lse=lsed)
-        p_mem = device_memory(pf, [qd, kd, vd, od, lsed], 0,
-                              pc.B * pc.Hq * pc.N * pc.N * 4)
+        def fn():
+            prefill(qd, kd, vd, causal=cfg.causal, scale=scale, out=od, lse=ld)
+        mem = device_memory(fn, [qd, kd, vd, od, ld], 0, cfg.B * cfg.Hq * cfg.N * cfg.N * 4)
+        return (q, k, v, scale), fn, od, ld, mem
 
-    dc = I.DECODE_GQA
-    if run_decode or run_paged:
+    def prefill_record(cfg, ms, mem, counters):
+        F = prefill_flops(cfg.B, cfg.Hq, cfg.N, cfg.d, cfg.causal)
+        st = stats(ms)
+        tf = F / (st["ms_avg"] * 1e-3) / 1e12
+        return dict(workload=cfg.name, **st, tflops=tf, tokens_per_s=cfg.B * cfg.N / (st["ms_avg"] * 1e-3),
+                    frac_of_peak=tf / PEAK_BF16_TFLOPS, flops_per_launch=F, device_memory=mem,
+                    roofline=mfma_roofline(PREFILL_KERNEL, tf, counters,
+                                           algorithmic_bytes=prefill_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d)))
+
+    # ------------------------------------------------ the step: 128K prefill + decode
+    pc, dc = I.PREFILL_GQA_128K, I.DECODE_GQA
+    run_p, run_d = want("prefill_gqa_128k"), want("decode")
+    if run_p:
+        host["c5"], pf, pod, pld, p_mem = prefill_setup(pc)
+    if run_d or leg("decode_paged"):
         dq, dk, dv, dl, dscale = I.decode_config_inputs(dc)
         lens_host = dl.tolist()
         dqd, dkd, dvd, dld = dq.to(dev), dk.to(dev), dv.to(dev), dl.to(dev)
-        dod = torch.empty_like(dqd)
         del dk, dv
-    if run_decode:
+        dod = torch.empty_like(dqd)
+    if run_d:
         ws = torch.empty(decode_workspace_bytes(dc.B, dc.Hq, dc.Hkv, dc.maxlen, dc.d), dtype=torch.uint8,
                          device=dev)
 
         def df():
             decode(dqd, dkd, dvd, dld, scale=dscale, out=dod, workspace=ws)
         d_mem = device_memory(df, [dqd, dkd, dvd, dld, dod], ws.numel(), None)
-    if run_paged:
-        # the same logical caches scattered over a shuffled pool of pages
+    if run_p or run_d:
+        for _ in range(args.warmup):
+            if run_p:
+                pf()
+            if run_d:
+                df()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            ev[i][0].record(stream)
+            if run_p:
+                pf()
+            ev[i][1].record(stream)
+            if run_d:
+                df()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        result["ms_per_step"] = (time.perf_counter() - t0) * 1e3 / K
+        p_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
+        d_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
+        result["config"] = {"workload": pc.name if run_p else dc.name,
+                            "step": "one prefill of this workload + one decode of decode.workload"}
+        if run_p:
+            rec = prefill_record(pc, p_ms, p_mem, "prefill_bf16_gqa128k_counters")
+            result["value"] = rec["tflops"]
+            result["config"].update({"B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "N": pc.N, "d": pc.d,
+                                     "causal": pc.causal})
+            result["roofline"] = rec.pop("roofline")
+            result["prefill"] = rec
+            host["c5_out"] = (pod.cpu(), pld.cpu())
+        if run_d:
+            nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d)
+            st = stats(d_ms)
+            gbs = nbytes / (st["ms_avg"] * 1e-3) / 1e9
+            result["decode"] = dict(workload=dc.name, **st, GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS,
+                                    bytes_per_launch=nbytes, tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
+                                    device_memory=d_mem,
+                                    roofline={"kernel": "decode_bf16_mfma_kernel + decode_combine_kernel",
+                                              "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                              "frac": gbs / PEAK_HBM_GBS,
+                                              "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
+                                              "rocprof": measured_counters("decode_gqa_counters", DECODE_SRC,
+                                                                           ("hbm_gbs_counter_run",
+                                                                            "shader_clock_ghz"))})
+            if result["value"] is None:
+                result["value"], result["unit"] = gbs, "GB/s"
+        if run_p:
+            del pf
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------ legs
+    legs_steps = max(1, K)
+    for name, cfg, counters, steps in (("prefill_mha_4k", I.PREFILL_MHA_4K, "prefill_bf16_mha4k_counters", legs_steps),
+                                       ("prefill_gqa_16k", I.PREFILL_GQA_16K, "prefill_bf16_gqa16k_counters",
+                                        max(1, min(K, 10)))):
+        if not leg(name):
+            continue
+        host[name], fn, od, ld, mem = prefill_setup(cfg)
+        for _ in range(min(args.warmup, 2)):
+            fn()
+        result[name] = prefill_record(cfg, time_calls(fn, stream, steps), mem, counters)
+        host[name + "_out"] = (od.cpu(), ld.cpu())
+        del fn, od, ld
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"] = result[name]["tflops"]
+
+    if leg("decode_paged"):
         kpd, vpd, table, _ = I.paged_cache(dkd, dvd, dl, args.page_size, seed=11)
         tbd = table.to(dev)
-        if not run_decode:
-            del dkd, dvd
+        del dkd, dvd
         pws = torch.empty(decode_paged_workspace_bytes(dc.B, dc.Hq, dc.Hkv, args.page_size, table.shape[1], dc.d),
                           dtype=torch.uint8, device=dev)
-        pod = torch.empty_like(dqd)
+        pgo = torch.empty_like(dqd)
 
         def pgf():
-            decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pod, workspace=pws)
+            decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pgo, workspace=pws)
+        for _ in range(args.warmup):
+            pgf()
+        st = stats(time_calls(pgf, stream, legs_steps))
+        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
+        gbs = nbytes / (st["ms_avg"] * 1e-3) / 1e9
+        result["decode_paged"] = dict(workload=dc.name + f"-paged{args.page_size}", page_size=args.page_size, **st,
+                                      GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS, bytes_per_launch=nbytes,
+                                      tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
+                                      roofline={"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
+                                                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                "frac": gbs / PEAK_HBM_GBS,
+                                                "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)})
+        del kpd, vpd, pws
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"], result["unit"] = gbs, "GB/s"
 
     # packed variable-length legs: a 4096-query chunk against a 16384-key prefix
     # (GQA B2 Hq32 Hkv8 d128, causal bottom-right), and the MHA 4K workload
     # with a 1024-key causal window
-    vl_legs = []
-    for name, on, lens, hq, hkv, causal, window in (
-            ("prefill_chunked", run_chunk, [(4096, 16384)] * 2, 32, 8, True, -1),
-            ("prefill_window", run_window, [(4096, 4096)] * 4, 32, 32, True, 1024)):
-        if not on:
+    for name, lens, hq, hkv, causal, window in (("prefill_chunked", [(4096, 16384)] * 2, 32, 8, True, -1),
+                                                ("prefill_window", [(4096, 4096)] * 4, 32, 32, True, 1024)):
+        if not leg(name):
             continue
         vq, vk, vv, cq, ck, vscale = I.varlen_inputs(lens, hq, hkv, 128, seed=5)
         vqd, vkd, vvd, cqd, ckd = vq.to(dev), vk.to(dev), vv.to(dev), cq.to(dev), ck.to(dev)
@@ -392,209 +508,91 @@ def main():
         vld = torch.empty((hq, vq.shape[0]), dtype=torch.float32, device=dev)
         mq = max(nq for nq, _ in lens)
 
-        def vf(vqd=vqd, vkd=vkd, vvd=vvd, cqd=cqd, ckd=ckd, vod=vod, vld=vld, mq=mq, causal=causal,
-               window=window, vscale=vscale):
-            prefill_varlen(vqd, vkd, vvd, cqd, ckd, mq, causal=causal, window_left=window, scale=vscale,
-                           out=vod, lse=vld)
+        def vf():
+            prefill_varlen(vqd, vkd, vvd, cqd, ckd, mq, causal=causal, window_left=window, scale=vscale, out=vod,
+                           lse=vld)
+        for _ in range(args.warmup):
+            vf()
+        st = stats(time_calls(vf, stream, legs_steps))
         flops = 4 * 128 * hq * varlen_pairs(lens, causal, window)
-        cfg = {"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128, "causal": causal,
-               "window_left": window}
-        waves = prefill_waves(128, causal, sum(nq for nq, _ in lens) / len(lens),
-                              sum(nk for _, nk in lens) / len(lens), window)
-        vl_legs.append((name, vf, flops, cfg, f"prefill_bf16_kernel<128,causal,varlen,{waves} waves>"))
+        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
+        result[name] = dict(config={"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128,
+                                    "causal": causal, "window_left": window}, **st, tflops=tf,
+                            flops_per_launch=flops,
+                            roofline=mfma_roofline("prefill_bf16_kernel<128, causal, varlen>", tf,
+                                                   name.replace("prefill_", "prefill_bf16_") + "_counters"))
+        del vqd, vkd, vvd, vod, vld
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"] = tf
 
-    if run_bwd:
+    if leg("backward"):
         # backward of the MHA 4K causal workload: the forward's o and lse feed it
-        bq, bk, bv, bdo, bscale = I.backward_inputs(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d, seed=1)
+        bc = I.PREFILL_MHA_4K
+        bq, bk, bv, bdo, bscale = I.backward_inputs(bc.B, bc.Hq, bc.Hkv, bc.N, bc.d, seed=1)
         bqd, bkd, bvd, bdod = bq.to(dev), bk.to(dev), bv.to(dev), bdo.to(dev)
         bo, blse = prefill(bqd, bkd, bvd, causal=True, scale=bscale)
         bdq, bdk, bdv = torch.empty_like(bqd), torch.empty_like(bkd), torch.empty_like(bvd)
-        bws = torch.empty(prefill_backward_workspace_bytes(pc.B, pc.Hq, pc.N), dtype=torch.uint8, device=dev)
+        bws = torch.empty(prefill_backward_workspace_bytes(bc.B, bc.Hq, bc.N), dtype=torch.uint8, device=dev)
 
         def bwf():
             prefill_backward(bqd, bkd, bvd, bo, bdod, blse, causal=True, scale=bscale, dq=bdq, dk=bdk, dv=bdv,
                              workspace=bws)
-        vl_legs.append(("backward", bwf, 2.5 * prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True),
-                        {"workload": pc.name, "flops": "2.5 x forward (five matrix products per score)",
-                         "kernels": "dQ (with the D and lse rows) + dK/dV"}, "bwd_dq + bwd_dkdv"))
-
-    for _ in range(args.warmup):
-        for _, vf, _, _, _ in vl_legs:
-            vf()
-        if run_prefill:
-            pf()
-        if run_decode:
-            df()
-        if run_paged:
-            pgf()
-    torch.cuda.synchronize()
-
-    # timed region: K steps, each = one prefill + one decode (+ one paged decode), events per call
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 + len(vl_legs))] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        for j, (_, vf, _, _, _) in enumerate(vl_legs):
-            ev[i][4 + j].record(stream)
-            vf()
-        ev[i][0].record(stream)
-        if run_prefill:
-            pf()
-        ev[i][1].record(stream)
-        if run_decode:
-            df()
-        ev[i][2].record(stream)
-        if run_paged:
-            pgf()
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    p_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
-    d_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
-    g_ms = sorted(ev[i][2].elapsed_time(ev[i][3]) for i in range(K))
-    vl_ms = []
-    for j in range(len(vl_legs)):
-        nxt = [(4 + j + 1) if j + 1 < len(vl_legs) else 0 for _ in range(K)]
-        vl_ms.append(sorted(ev[i][4 + j].elapsed_time(ev[i][nxt[i]]) for i in range(K)))
-    p_avg = sum(p_ms) / K
-    d_avg = sum(d_ms) / K
-    g_avg = sum(g_ms) / K
+        for _ in range(args.warmup):
+            bwf()
+        st = stats(time_calls(bwf, stream, legs_steps))
+        flops = 2.5 * prefill_flops(bc.B, bc.Hq, bc.N, bc.d, True)
+        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
+        result["backward"] = dict(config={"workload": bc.name, "flops": "2.5 x forward (five matrix products per "
+                                                                        "score)",
+                                          "kernels": "dQ (with the D and lse rows) + dK/dV"}, **st, tflops=tf,
+                                  flops_per_launch=flops,
+                                  roofline=mfma_roofline("bwd_dq_kernel + bwd_dkdv_kernel", tf, "backward_counters",
+                                                         src=BACKWARD_SRC))
+        if result["value"] is None:
+            result["value"] = tf
 
     props = torch.cuda.get_device_properties(dev)
-    result = {
-        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV-read GB/s (% HBM)",
-        "value": None,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / K,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) rounded to bf16)",
-        "config": {"workload": pc.name, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "N": pc.N, "d": pc.d,
-                   "causal": pc.causal, "step": "one prefill (this workload) + one decode (decode.workload) + one paged decode "
-                                                              "(decode_paged.workload) + the prefill_chunked and "
-                                                              "prefill_window legs"},
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", ""), "torch": torch.__version__,
-                   "hip": getattr(torch.version, "hip", None)},
-    }
-    if run_prefill:
-        F = prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True)
-        tflops = F / (p_avg * 1e-3) / 1e12
-        result["value"] = tflops
-        result["prefill"] = {"ms_avg": p_avg, "ms_median": p_ms[K // 2], "ms_min": p_ms[0],
-                             "tflops": tflops, "tokens_per_s": pc.B * pc.N / (p_avg * 1e-3),
-                             "frac_of_peak": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": F}
-        traffic = measured_traffic("prefill_bf16_mha4k_counters", PREFILL_SRC)
-        result["roofline"] = {"kernel": f"prefill_bf16_kernel<128,causal,{prefill_waves(pc.d, True, pc.N, pc.N)} waves>",
-                              "bound": "mfma",
-                              "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                              "algorithmic_bytes": prefill_bytes(pc.B, pc.Hq, pc.Hkv, pc.N, pc.d),
-                              "rocprof": measured_counters("prefill_bf16_mha4k_counters", PREFILL_SRC,
-                                                           ("mfma_busy_fraction", "mfma_flops_over_algorithmic",
-                                                            "shader_clock_ghz"))}
-        result["prefill"]["device_memory"] = p_mem
-    if run_decode:
-        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d)
-        gbs = nbytes / (d_avg * 1e-3) / 1e9
-        result["decode"] = {"workload": dc.name, "ms_avg": d_avg, "ms_median": d_ms[K // 2],
-                            "ms_min": d_ms[0], "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
-                            "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (d_avg * 1e-3),
-                            "roofline": {"kernel": "decode_bf16_mfma_kernel + decode_combine_kernel",
-                                         "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                         "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
-                                         "rocprof": measured_counters("decode_gqa_counters", DECODE_SRC,
-                                                                      ("hbm_gbs_counter_run", "shader_clock_ghz"))},
-                            "device_memory": d_mem}
-        if result["value"] is None:
-            result["value"], result["unit"] = gbs, "GB/s"
-    for (name, _, flops, cfg, kernel), ms in zip(vl_legs, vl_ms):
-        avg = sum(ms) / K
-        tf = flops / (avg * 1e-3) / 1e12
-        result[name] = {"config": cfg, "ms_avg": avg, "ms_median": ms[K // 2], "ms_min": ms[0], "tflops": tf,
-                        "flops_per_launch": flops,
-                        "roofline": {"kernel": kernel, "bound": "mfma",
-                                     "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                     "frac": tf / PEAK_BF16_TFLOPS}}
-        if result["value"] is None:
-            result["value"] = tf
-    if run_paged:
-        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
-        gbs = nbytes / (g_avg * 1e-3) / 1e9
-        result["decode_paged"] = {"workload": dc.name + f"-paged{args.page_size}", "page_size": args.page_size,
-                                  "ms_avg": g_avg, "ms_median": g_ms[K // 2], "ms_min": g_ms[0],
-                                  "GB_per_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
-                                  "bytes_per_launch": nbytes, "tokens_per_s": dc.B / (g_avg * 1e-3),
-                                  "roofline": {"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
-                                               "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
-        if result["value"] is None:
-            result["value"], result["unit"] = gbs, "GB/s"
-    # the other two causal GQA configurations, timed after the steps above
-    # with their own (smaller) step counts: B2 Hq32 Hkv8 N16384 and
-    # B1 Hq64 Hkv8 N131072 (O(N) memory: no N x N buffer exists anywhere)
-    cfg_legs = []
-    for name, cfg, steps in (("prefill_gqa_16k", I.PREFILL_GQA_16K, max(1, min(K, 10))),
-                             ("prefill_gqa_128k", I.PREFILL_GQA_128K, max(1, min(K, 3)))):
-        if not (args.only == name or (args.only is None and not args.no_configs)):
-            continue
-        cq, ck_, cv, cscale = I.prefill_config_inputs(cfg)
-        cqd, ckd_, cvd = cq.to(dev), ck_.to(dev), cv.to(dev)
-        del cq, ck_, cv
-        cod = torch.empty_like(cqd)
-        cld = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
-        prefill(cqd, ckd_, cvd, causal=True, scale=cscale, out=cod, lse=cld)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            prefill(cqd, ckd_, cvd, causal=True, scale=cscale, out=cod, lse=cld)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-        avg = sum(ms) / steps
-        F = prefill_flops(cfg.B, cfg.Hq, cfg.N, cfg.d, True)
-        tf = F / (avg * 1e-3) / 1e12
-        result[name] = {"workload": cfg.name, "steps": steps, "ms_avg": avg, "ms_median": ms[steps // 2],
-                        "ms_min": ms[0], "tflops": tf, "tokens_per_s": cfg.B * cfg.N / (avg * 1e-3),
-                        "flops_per_launch": F,
-                        "roofline": {"kernel": f"prefill_bf16_kernel<128,causal,{prefill_waves(cfg.d, True, cfg.N, cfg.N)} waves>",
-                                     "bound": "mfma", "achieved": tf,
-                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}
-        cfg_legs.append(name)
-        del cqd, ckd_, cvd, cod, cld
-        torch.cuda.empty_cache()
-        if result["value"] is None:
-            result["value"] = tf
-    if args.only is None and not args.no_ceilings:
-        ceil = measured_ceilings()
-        result["ceilings"] = ceil
-        if ceil is not None:
-            sus = ceil["mfma_bf16_random_operands"]["tflops"]
-            for rl in ([result.get("roofline")] + [result[n]["roofline"] for n, _, _, _, _ in vl_legs]
-                       + [result[n]["roofline"] for n in cfg_legs]):
-                if rl is not None:
-                    rl["measured_ceiling"] = sus
-                    rl["frac_of_measured_ceiling"] = rl["achieved"] / sus
-            for leg in ("decode", "decode_paged"):
-                if leg in result:
-                    rl = result[leg]["roofline"]
-                    rl["measured_ceiling"] = ceil["hbm_read_gbs"]
-                    rl["frac_of_measured_ceiling"] = rl["achieved"] / ceil["hbm_read_gbs"]
-    if run_prefill and not args.no_cpu_baseline:
-        if pool is not None:
-            result["cpu_baseline"] = cpu_baseline_pool(pool, workers, q, k, v, scale, od.cpu(), lsed.cpu())
-            pool.close()
-            pool.join()
-        else:
-            result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_seconds, od.cpu(), lsed.cpu())
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "arch": getattr(props, "gcnArchName", ""), "torch": torch.__version__,
+                        "hip": getattr(torch.version, "hip", None)}
+    if only is None and not args.no_ceilings:
+        result["ceilings"] = measured_ceilings()
+
+    # ------------------------------------------------ oracle: cpu_baseline and parity of the timed outputs
+    if pool is not None:
+        parity = {}
+        if "c5_out" in host:
+            q, k, v, scale = host["c5"]
+            rows = c5_sample_rows(pc.N)
+            err, flops, dt = oracle_check(pool, q, k, v, scale, *host["c5_out"], rows, heads_per_job=4)
+            rate = flops / dt
+            full = prefill_flops(pc.B, pc.Hq, pc.N, pc.d, True)
+            result["cpu_baseline"] = {
+                "value": rate / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+                "host_cpu_count": os.cpu_count(), "host_affinity_cores": len(os.sched_getaffinity(0)),
+                "sample": f"{len(rows)} causal query rows (first/last rows, 64-multiples +-1 below 1024, powers of "
+                          f"two +-1, seeded uniform rows) of each of the {pc.B * pc.Hq} heads of the {pc.name} "
+                          f"workload, fp64 numpy oracle, {workers} worker processes with 1 BLAS thread each, "
+                          f"{dt:.1f} s wall (inputs pickled to the workers inside the timed span); the rate is the "
+                          f"algorithmic FLOPs of those rows over wall time",
+                "sample_flops": flops, "sample_seconds": dt,
+                "extrapolated_full_workload_seconds": full / rate,
+                "extrapolated_note": "extrapolated: the measured rate applied to the whole workload's algorithmic "
+                                     "FLOPs, not timed",
+                "gpu_speedup_over_oracle": result["value"] * 1e12 / rate if result["value"] else None}
+            parity[pc.name] = dict(rows=f"{len(rows)} sampled rows x {pc.B * pc.Hq} heads", bar=BAR, **err)
+        for name, cfg in (("prefill_gqa_16k", I.PREFILL_GQA_16K), ("prefill_mha_4k", I.PREFILL_MHA_4K)):
+            if name + "_out" not in host:
+                continue
+            q, k, v, scale = host[name]
+            err, flops, dt = oracle_check(pool, q, k, v, scale, *host[name + "_out"], range(cfg.N),
+                                          heads_per_job=1)
+            parity[cfg.name] = dict(rows=f"all {cfg.N} rows x {cfg.B * cfg.Hq} heads", bar=BAR, oracle_seconds=dt,
+                                    **err)
+        pool.close()
+        pool.join()
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 

@@ -49,7 +49,7 @@
 namespace fa {
 namespace {
 
-constexpr int kChunk = kDecodeChunk;  // keys per split
+constexpr int kChunk = kDecodeChunk;  // keys per split of the fp32 path
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = kChunk / kWaves;  // 128
 
@@ -77,15 +77,7 @@ __device__ __forceinline__ int split_of_block(int nsplit) {
 template <typename T>
 struct Elem;
 template <>
-struct Elem<uint16_t> {  // bf16 storage
-  __device__ static inline void widen(const u32x4& w, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16lo_to_f32(w[i]);
-      f[2 * i + 1] = bf16hi_to_f32(w[i]);
-    }
-  }
-  __device__ static inline float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+struct Elem<uint16_t> {  // bf16 storage: only the combine's output store
   __device__ static inline void store1(uint16_t* p, float x) {
     *p = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
   }

@@ -45,7 +45,9 @@ float softmax_coeff(float scale) {
 int check_common(int B, int Hq, int Hkv, int d, float scale) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  // the kernels exponentiate in base 2 with the coefficient |scale| log2(e),
+  // which must itself be a finite fp32 number
+  if (!std::isfinite(scale) || !std::isfinite(std::fabs(scale) * fa::kLog2e)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }

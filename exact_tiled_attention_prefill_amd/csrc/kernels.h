@@ -92,7 +92,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
-// Keys per split-KV chunk in decode.
+// Keys per split-KV chunk of the fp32 decode path (the bf16 path picks its
+// chunk per launch).
 constexpr int kDecodeChunk = 512;
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
 

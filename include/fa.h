@@ -38,6 +38,12 @@
  *     is no silent fallback: the caller decides what to do.
  *   - Calls are thread-safe; the library holds no mutable global state other
  *     than a per-device architecture cache.
+ *   - scale: any finite fp32 value whose softmax coefficient |scale|*log2(e)
+ *     is finite in fp32 (|scale| below about 2.3e38; larger values return
+ *     FA_ERR_INVALID_ARG).  The kernels form scale * (q . k) in fp32, so every
+ *     scaled score of a visible (query, key) pair must also be finite in fp32;
+ *     if one overflows, the outputs of that row are unspecified (NaN in
+ *     practice).  Non-finite input values likewise give unspecified results.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -51,8 +57,9 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, Hq % Hkv != 0, non-finite
-                             scale, misaligned pointer, too-small workspace */
+  FA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, Hq % Hkv != 0, scale not
+                             finite or |scale|*log2(e) not finite in fp32,
+                             misaligned pointer, too-small workspace */
   FA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, or device is not gfx950 */
   FA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
   FA_ERR_NO_MEMORY = 4    /* stream-ordered workspace allocation failed */
@@ -129,7 +136,8 @@ int fa_prefill_varlen(const void* q, const void* k, const void* v, void* o,
  * be NULL (obtained stream-ordered) or hold at least
  * fa_prefill_backward_workspace_bytes(B, Hq, N) bytes, 256-byte aligned.
  * Every output element is written by exactly one workgroup (no atomics), so
- * the results are deterministic.  Work: three kernel launches on `stream`.
+ * the results are deterministic.  Work: two kernel launches on `stream` (dQ
+ * with the rows' rowsum(dout * o) terms, then dK/dV).
  */
 int fa_prefill_backward(const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse,

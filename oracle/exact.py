@@ -107,15 +107,18 @@ def attention(q, k, v, causal, scale):
     return o, lse
 
 
-def attention_rows(q, k, v, causal, scale, rows, heads=None):
+def attention_rows(q, k, v, causal, scale, rows, heads=None, rows_per_block=256):
     """The same definition evaluated only at query rows `rows` (and heads).
 
-    Softmax is per row, so each requested row is computed on its own: its
-    score row against the keys it may see (0..i when causal, all otherwise),
-    its max, exp, sum and weighted sum of V.  q/k/v may be torch CPU tensors
-    (converted head by head to keep memory bounded).  `heads` is a list of
-    (b, h) pairs; default all.  Returns (o [len(heads), len(rows), d],
-    lse [len(heads), len(rows)]).
+    Softmax is per row, so the requested rows are independent of the others:
+    for a group of up to `rows_per_block` of them the score rows
+    S[rows, :] = scale * q[rows] k^T are materialised (against keys
+    0 .. the group's last row when causal, all keys otherwise), entries with
+    key index j > i are set to -inf under the causal mask, and each row takes
+    its max, exp, sum and weighted sum of V -- `attention` restricted to those
+    rows.  q/k/v may be torch CPU tensors (converted head by head to keep
+    memory bounded).  `heads` is a list of (b, h) pairs; default all.
+    Returns (o [len(heads), len(rows), d], lse [len(heads), len(rows)]).
     """
     bsz, hq, n, d = q.shape
     hkv = k.shape[1]
@@ -132,14 +135,13 @@ def attention_rows(q, k, v, causal, scale, rows, heads=None):
             kv_cache[(b, g)] = (_f64(k[b, g]), _f64(v[b, g]))
         kb, vb = kv_cache[(b, g)]
         qb = _f64(q[b, h][rows])
-        for r, i in enumerate(rows):
-            nk = int(i) + 1 if causal else n
-            s = float(scale) * (kb[:nk] @ qb[r])
-            m = s.max()
-            p = np.exp(s - m)
-            l = p.sum()
-            o[t, r] = (p @ vb[:nk]) / l
-            lse[t, r] = m + math.log(l)
+        for r0 in range(0, len(rows), rows_per_block):
+            ri = rows[r0:r0 + rows_per_block]
+            nk = int(ri.max()) + 1 if causal else n
+            s = float(scale) * (qb[r0:r0 + len(ri)] @ kb[:nk].T)
+            if causal:
+                s[np.arange(nk)[None, :] > ri[:, None]] = -np.inf
+            o[t, r0:r0 + len(ri)], lse[t, r0:r0 + len(ri)] = _softmax_rows_times_v(s, vb[:nk])
     return o, lse
 
 

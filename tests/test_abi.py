@@ -78,6 +78,8 @@ def prefill_call(fn, **kw):
     (dict(Hq=6, Hkv=4), binding.FA_ERR_INVALID_ARG),
     (dict(causal=2), binding.FA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=3e38), binding.FA_ERR_INVALID_ARG),    # |scale| log2(e) overflows fp32
+    (dict(scale=-3e38), binding.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
     (dict(q=P_MIS), binding.FA_ERR_INVALID_ARG),
     (dict(o=P_MIS), binding.FA_ERR_INVALID_ARG),
@@ -114,6 +116,7 @@ def decode_call(fn, ws=False, **kw):
     (dict(maxlen=0), binding.FA_ERR_INVALID_ARG),
     (dict(Hq=8, Hkv=3), binding.FA_ERR_INVALID_ARG),
     (dict(scale=float("-inf")), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=2.5e38), binding.FA_ERR_INVALID_ARG),  # |scale| log2(e) overflows fp32
     (dict(k=P_MIS), binding.FA_ERR_INVALID_ARG),
     (dict(sl=ctypes.c_void_p(0x10001)), binding.FA_ERR_INVALID_ARG),
     (dict(B=70000), binding.FA_ERR_INVALID_ARG),

@@ -275,17 +275,19 @@ def test_matches_torch_sdpa_float64(B, hkv, G, n, d, causal, scale, seed):
     assert np.abs(o - ref).max() <= 1e-12
 
 
-def test_rows_variant_matches_full():
-    """attention_rows evaluates the same definition at chosen rows and heads."""
+@pytest.mark.parametrize("per_block", [1, 2, 256])
+@pytest.mark.parametrize("rows", [[0, 1, 17, 48, 49], [49, 3, 17, 0, 30, 2]])
+def test_rows_variant_matches_full(per_block, rows):
+    """attention_rows evaluates the same definition at chosen rows and heads,
+    whatever the rows' order and however they are grouped."""
     q, k, v, scale = prefill_inputs(2, 4, 2, 50, 16, "bf16", seed=5)
     o, lse = oracle.attention(q, k, v, True, scale)
-    rows = [0, 1, 17, 48, 49]
     heads = [(0, 0), (1, 3), (0, 2)]
-    orr, lr = oracle.attention_rows(q, k, v, True, scale, rows, heads)
+    orr, lr = oracle.attention_rows(q, k, v, True, scale, rows, heads, rows_per_block=per_block)
     for t, (b, h) in enumerate(heads):
         assert np.abs(orr[t] - o[b, h, rows]).max() <= 1e-13
         assert np.abs(lr[t] - lse[b, h, rows]).max() <= 1e-13
-    on, ln_ = oracle.attention_rows(q, k, v, False, scale, rows, heads)
+    on, ln_ = oracle.attention_rows(q, k, v, False, scale, rows, heads, rows_per_block=per_block)
     of, lf = oracle.attention(q, k, v, False, scale)
     for t, (b, h) in enumerate(heads):
         assert np.abs(on[t] - of[b, h, rows]).max() <= 1e-13
@@ -533,6 +535,77 @@ def test_varlen_rows_without_keys_and_chunking():
     o, lse = oracle.attention_varlen(qp[:8], kp[:5], vp[:5], [0, 8], [0, 5], True, scale)
     assert np.all(o[:3] == 0) and np.all(np.isneginf(lse[:, :3]))
     assert np.isfinite(lse[:, 3:]).all()
+
+
+@pytest.mark.parametrize("lens", [[(5, 9), (7, 7), (12, 3)], [(16, 40), (33, 33), (50, 20)]])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1)])
+def test_varlen_noncausal_matches_torch_sdpa(lens, hq, hkv):
+    """P20b: without the causal mask and without a window every row sees all
+    n_k keys of its sequence, whatever n_q is: the rows equal PyTorch CPU
+    float64 SDPA with no mask, sequence by sequence (GQA by repeating K/V
+    heads), including sequences with more queries than keys."""
+    d, scale = 8, 0.37
+    qs = [rand((nq, hq, d), 130 + i) for i, (nq, _) in enumerate(lens)]
+    ks = [rand((nk, hkv, d), 230 + i) for i, (_, nk) in enumerate(lens)]
+    vs = [rand((nk, hkv, d), 330 + i) for i, (_, nk) in enumerate(lens)]
+    q, k, cu_q, cu_k = _pack(qs, ks)
+    v = np.concatenate(vs)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, False, scale)
+    for b, (nq, nk) in enumerate(lens):
+        tq = torch.from_numpy(qs[b]).permute(1, 0, 2)[None]
+        tk = torch.from_numpy(np.repeat(ks[b], hq // hkv, axis=1)).permute(1, 0, 2)[None]
+        tv = torch.from_numpy(np.repeat(vs[b], hq // hkv, axis=1)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0].permute(1, 0, 2).numpy()
+        assert np.abs(o[cu_q[b]:cu_q[b + 1]] - ref).max() <= 1e-12
+        # lse: log of the row's sum of exp(scale q.k), by logsumexp of torch
+        s = scale * torch.einsum("qhd,khd->hqk", torch.from_numpy(qs[b]),
+                                 torch.from_numpy(np.repeat(ks[b], hq // hkv, axis=1)))
+        assert np.abs(lse[:, cu_q[b]:cu_q[b + 1]] - torch.logsumexp(s, dim=-1).numpy()).max() <= 1e-12
+
+
+# sequences (n_q, n_k) with the queries at the end (off > 0), aligned (off = 0)
+# and with more queries than keys (off < 0, the window bound moves left)
+NONCAUSAL_WINDOW_LENS = [(7, 12), (6, 6), (9, 5)]
+
+
+@pytest.mark.parametrize("w", [0, 1, 3, 50])
+def test_varlen_noncausal_window_identical_keys_give_tail_mean(w):
+    """P22b: without the causal mask a window W >= 0 is left-only: row i of a
+    sequence sees keys max(0, i + off - W) .. n_k - 1 with off = n_k - n_q
+    (the queries are the last n_q positions).  With identical keys the weights
+    are uniform over that range: o = the mean of those V rows and
+    lse = s + ln(count) (closed form).  Every row keeps at least key n_k - 1,
+    since i + off - W <= n_k - 1."""
+    d, scale = 4, 0.3
+    qs = [rand((nq, 1, d), 430 + i) for i, (nq, _) in enumerate(NONCAUSAL_WINDOW_LENS)]
+    key = rand((1, 1, d), 440)
+    ks = [np.repeat(key, nk, axis=0) for _, nk in NONCAUSAL_WINDOW_LENS]
+    vs = [rand((nk, 1, d), 450 + i) for i, (_, nk) in enumerate(NONCAUSAL_WINDOW_LENS)]
+    q, k, cu_q, cu_k = _pack(qs, ks)
+    v = np.concatenate(vs)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, False, scale, window_left=w)
+    for b, (nq, nk) in enumerate(NONCAUSAL_WINDOW_LENS):
+        for i in range(nq):
+            lo = max(0, i + nk - nq - w)
+            row = cu_q[b] + i
+            assert np.abs(o[row, 0] - vs[b][lo:, 0].mean(axis=0)).max() <= 1e-14
+            assert abs(lse[0, row] - (scale * qs[b][i, 0] @ key[0, 0] + math.log(nk - lo))) <= 1e-13
+
+
+def test_pins_catch_noncausal_window_from_row_index(monkeypatch):
+    """A non-causal window measured from the packed row index i instead of the
+    row's position i + off fails P22b (off != 0 for two of its sequences)."""
+    real = oatt.varlen_visible
+
+    def wrong(i, nq, nk, causal, w):
+        lo, hi = real(i, nq, nk, causal, w)
+        if not causal and w >= 0:
+            lo = max(0, i - w)
+        return lo, hi
+
+    monkeypatch.setattr(oatt, "varlen_visible", wrong)
+    with pytest.raises(AssertionError):
+        test_varlen_noncausal_window_identical_keys_give_tail_mean(1)
 
 
 def test_pins_catch_window_off_by_one(monkeypatch):

@@ -93,7 +93,7 @@ def test_paged_ids_outside_pool_are_clamped():
 
 @pytest.mark.parametrize("page", [16, 64])
 def test_paged_decode_workload(page):
-    """The B64 Hq32 Hkv8 d128 decode workload (2048-key chunks) in 16- and
+    """The B64 Hq32 Hkv8 d128 decode workload (4096-key chunks) in 16- and
     64-key pages -- 16-key pages give the most page ids per chunk: bit-identical
     to contiguous decode, and against the oracle on sampled sequences."""
     cfg = I.DECODE_GQA

@@ -18,6 +18,7 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_ERR_NO_MEMORY = 4
+FA_ERR_TOO_LARGE = 5
 
 # name -> (restype, argtypes); the exported symbols of include/fa.h
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -38,6 +39,7 @@ SIGNATURES = {
     "fa_prefill_backward_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_paged_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
 }
 
 _lib = None
@@ -202,6 +204,34 @@ def decode(q, kcache, vcache, seqlens, scale=None, out=None, workspace=None, str
         fn = lib.fa_decode_ws if bf16 else lib.fa_decode_f32_ws
         st = fn(*args, _ptr(workspace), workspace.numel(), _stream_ptr(stream))
     _check(st, fn.__name__)
+    return out
+
+
+def decode_noalloc(q, kcache, vcache, seqlens, scale=None, out=None, stream=None):
+    """decode() through fa_decode_noalloc (bf16): the library allocates no
+    device memory; its partials go to a fixed per-GPU array (calls that can
+    overlap on one GPU race on it).  Raises FaError(FA_ERR_TOO_LARGE) when the
+    sizes exceed that array.  Returns o [B,Hq,d]."""
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(kcache, "kcache", torch.bfloat16, 4)
+    _require(vcache, "vcache", torch.bfloat16, 4)
+    _require(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, d = q.shape
+    _, Hkv, maxlen, _ = kcache.shape
+    if tuple(kcache.shape) != (B, Hkv, maxlen, d) or tuple(vcache.shape) != (B, Hkv, maxlen, d):
+        raise ValueError("kcache/vcache must be [B, Hkv, maxlen, d] matching q")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must be [B]")
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3)
+    st = load_library().fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(out), B, Hq,
+                                          Hkv, maxlen, d, float(scale), _stream_ptr(stream))
+    _check(st, "fa_decode_noalloc")
     return out
 
 

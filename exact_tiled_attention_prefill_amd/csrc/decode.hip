@@ -43,6 +43,8 @@
 //     once.
 // seqlens is read only on the device; chunks at or past a sequence's length
 // exit at once, rows past the length are never loaded.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -768,6 +770,43 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
   if (a.d == 128) return launch_g<float, 128>(a, stream);
   if (a.d == 64) return launch_g<float, 64>(a, stream);
   return hipErrorInvalidValue;
+}
+
+size_t decode_noalloc_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
+  return partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen));
+}
+
+}  // namespace fa
+
+// Fixed partials array of the allocation-free decode entry point.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.  Every partial the combine reads is
+// written by the split kernel of the same call, so nothing needs clearing.
+static __device__ __align__(256) uint8_t scratch[fa::kDecodeScratchBytes];
+
+namespace fa {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -141,6 +141,8 @@ const char* fa_strerror(int status) {
       return "FA_ERR_HIP: HIP runtime or launch failure";
     case FA_ERR_NO_MEMORY:
       return "FA_ERR_NO_MEMORY: workspace allocation failed";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: sizes exceed the fixed scratch of fa_decode_noalloc";
     default:
       return "unknown fa_status";
   }
@@ -249,6 +251,20 @@ int fa_decode_ws(const void* q, const void* kcache, const void* vcache, const in
   if (workspace == nullptr) return FA_ERR_INVALID_ARG;
   return decode_run(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale, workspace, workspace_bytes,
                     stream, true);
+}
+
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* seqlens, void* o,
+                      int B, int Hq, int Hkv, int maxlen, int d, float scale, void* stream) {
+  int st = decode_check(q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, scale);
+  if (st != FA_OK) return st;
+  if (fa::decode_noalloc_bytes(B, Hq, Hkv, maxlen, d) > fa::kDecodeScratchBytes) return FA_ERR_TOO_LARGE;
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  if (fa::decode_scratch_address(&ws) != hipSuccess) return FA_ERR_HIP;
+  fa::DecodeArgs a{q, kcache, vcache, seqlens, o, B, Hq, Hkv, maxlen, d, softmax_coeff(scale), scale < 0.f, ws,
+                   fa::kDecodeScratchBytes, fa::PagedKV{}};
+  return fa::launch_decode_bf16(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int page_size, int max_pages, int d) {

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/fa.h"
+
 namespace fa {
 
 // Softmax runs in base 2: exp(scale*s) = exp2(c*s) with c = |scale|*log2(e),
@@ -96,5 +98,13 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 // chunk per launch).
 constexpr int kDecodeChunk = 512;
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
+
+// Allocation-free bf16 decode: the partials live in a fixed device array of
+// kDecodeScratchBytes (one per GPU, for the life of the process).
+constexpr size_t kDecodeScratchBytes = FA_DECODE_NOALLOC_SCRATCH_BYTES;
+// Bytes of that array a bf16 decode of these sizes uses.
+size_t decode_noalloc_bytes(int B, int Hq, int Hkv, int maxlen, int d);
+// Device address of the current device's array (looked up once per device).
+hipError_t decode_scratch_address(void** ptr);
 
 }  // namespace fa

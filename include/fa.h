@@ -62,7 +62,9 @@ typedef enum {
                              misaligned pointer, too-small workspace */
   FA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, or device is not gfx950 */
   FA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
-  FA_ERR_NO_MEMORY = 4    /* stream-ordered workspace allocation failed */
+  FA_ERR_NO_MEMORY = 4,   /* stream-ordered workspace allocation failed */
+  FA_ERR_TOO_LARGE = 5    /* fa_decode_noalloc: the sizes need more than its
+                             fixed FA_DECODE_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -194,6 +196,31 @@ int fa_decode_f32_ws(const float* q, const float* kcache, const float* vcache,
 /* Workspace bytes fa_decode_ws / fa_decode_f32_ws need for these sizes
  * (0 if the sizes are invalid). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
+
+/*
+ * fa_decode (bf16) for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layouts, semantics and kernels as fa_decode,
+ * and bit-identical results; the split-KV partials go to a fixed device array
+ * of FA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipMallocAsync or hipFree) and enqueues exactly the two kernels of
+ * fa_decode_ws.
+ *   Limit: the partials take (B*Hq*S*d*4 and B*Hq*S*4 bytes, each rounded up
+ *   to 256) for the S key chunks the launcher picks; sizes beyond the array
+ *   return FA_ERR_TOO_LARGE before any HIP call.  It always fits when
+ *   fa_decode_workspace_bytes(B, Hq, Hkv, maxlen, d) <=
+ *   FA_DECODE_NOALLOC_SCRATCH_BYTES (e.g. B 64, Hq 32, Hkv 8, maxlen 32768,
+ *   d 128 uses 8.5 MB).
+ *   Sharing: every call on one GPU uses that GPU's single array.  Calls on
+ *   the same stream are ordered and safe; calls that can overlap on one GPU
+ *   (other streams, other host threads) race on it and must be serialised by
+ *   the caller.  Nothing in the array needs clearing between calls.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* seqlens, void* o, int B, int Hq, int Hkv,
+                      int maxlen, int d, float scale, void* stream);
 
 /*
  * Decode against a paged KV cache.  The retained history stays available to

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_strerror_and_version():
     lib = binding.load_library()
-    for code in range(5):
+    for code in range(6):
         assert lib.fa_strerror(code).decode().startswith("FA_")
     assert b"unknown" in lib.fa_strerror(99)
     assert lib.fa_version() >= 100
@@ -235,3 +235,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(binding.FaError):
         binding.load_library()
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), binding.FA_ERR_INVALID_ARG),
+    (dict(sl=None), binding.FA_ERR_INVALID_ARG),
+    (dict(Hq=8, Hkv=3), binding.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), binding.FA_ERR_INVALID_ARG),
+    (dict(d=80), binding.FA_ERR_UNSUPPORTED),
+    (dict(B=4096, Hq=64, Hkv=8, maxlen=65536), binding.FA_ERR_TOO_LARGE),
+    (dict(B=60000, Hq=32, Hkv=8, maxlen=1 << 20), binding.FA_ERR_TOO_LARGE),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(kw, code):
+    """fa_decode_noalloc: invalid arguments, and sizes whose partials exceed
+    its fixed array, are refused on the host (no device here)."""
+    assert decode_call(binding.load_library().fa_decode_noalloc, **kw) == code

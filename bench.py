@@ -278,6 +278,20 @@ def time_calls(fn, stream, steps):
     return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
 
 
+def warm(fn, calls, seconds=0.2):
+    """Untimed warm-up: at least `calls` calls and `seconds` of wall time, so
+    that the GPU's clocks have left their idle state before timing starts."""
+    import torch
+
+    t0, n = time.perf_counter(), 0
+    while n < calls or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def stats(ms):
     k = len(ms)
     return {"ms_avg": sum(ms) / k, "ms_median": ms[k // 2], "ms_min": ms[0], "launches": k}
@@ -381,17 +395,115 @@ def main():
                     roofline=mfma_roofline(PREFILL_KERNEL, tf, counters,
                                            algorithmic_bytes=prefill_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d)))
 
-    # ------------------------------------------------ the step: 128K prefill + decode
     pc, dc = I.PREFILL_GQA_128K, I.DECODE_GQA
     run_p, run_d = want("prefill_gqa_128k"), want("decode")
-    if run_p:
-        host["c5"], pf, pod, pld, p_mem = prefill_setup(pc)
     if run_d or leg("decode_paged"):
         dq, dk, dv, dl, dscale = I.decode_config_inputs(dc)
         lens_host = dl.tolist()
         dqd, dkd, dvd, dld = dq.to(dev), dk.to(dev), dv.to(dev), dl.to(dev)
         del dk, dv
         dod = torch.empty_like(dqd)
+    # ------------------------------------------------ legs, timed before the step: after seconds of
+    # sustained 128K prefill the part runs hot and clocks lower, which would
+    # penalise the short legs
+    legs_steps = max(1, K)
+    for name, cfg, counters, steps in (("prefill_mha_4k", I.PREFILL_MHA_4K, "prefill_bf16_mha4k_counters", legs_steps),
+                                       ("prefill_gqa_16k", I.PREFILL_GQA_16K, "prefill_bf16_gqa16k_counters",
+                                        max(1, min(K, 10)))):
+        if not leg(name):
+            continue
+        host[name], fn, od, ld, mem = prefill_setup(cfg)
+        warm(fn, args.warmup)
+        result[name] = prefill_record(cfg, time_calls(fn, stream, steps), mem, counters)
+        host[name + "_out"] = (od.cpu(), ld.cpu())
+        del fn, od, ld
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"] = result[name]["tflops"]
+
+    if leg("decode_paged"):
+        kpd, vpd, table, _ = I.paged_cache(dkd, dvd, dl, args.page_size, seed=11)
+        tbd = table.to(dev)
+        pws = torch.empty(decode_paged_workspace_bytes(dc.B, dc.Hq, dc.Hkv, args.page_size, table.shape[1], dc.d),
+                          dtype=torch.uint8, device=dev)
+        pgo = torch.empty_like(dqd)
+
+        def pgf():
+            decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pgo, workspace=pws)
+        warm(pgf, args.warmup)
+        st = stats(time_calls(pgf, stream, legs_steps))
+        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
+        gbs = nbytes / (st["ms_avg"] * 1e-3) / 1e9
+        result["decode_paged"] = dict(workload=dc.name + f"-paged{args.page_size}", page_size=args.page_size, **st,
+                                      GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS, bytes_per_launch=nbytes,
+                                      tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
+                                      roofline={"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
+                                                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                "frac": gbs / PEAK_HBM_GBS,
+                                                "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)})
+        del kpd, vpd, pws
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"], result["unit"] = gbs, "GB/s"
+
+    # packed variable-length legs: a 4096-query chunk against a 16384-key prefix
+    # (GQA B2 Hq32 Hkv8 d128, causal bottom-right), and the MHA 4K workload
+    # with a 1024-key causal window
+    for name, lens, hq, hkv, causal, window in (("prefill_chunked", [(4096, 16384)] * 2, 32, 8, True, -1),
+                                                ("prefill_window", [(4096, 4096)] * 4, 32, 32, True, 1024)):
+        if not leg(name):
+            continue
+        vq, vk, vv, cq, ck, vscale = I.varlen_inputs(lens, hq, hkv, 128, seed=5)
+        vqd, vkd, vvd, cqd, ckd = vq.to(dev), vk.to(dev), vv.to(dev), cq.to(dev), ck.to(dev)
+        vod = torch.empty_like(vqd)
+        vld = torch.empty((hq, vq.shape[0]), dtype=torch.float32, device=dev)
+        mq = max(nq for nq, _ in lens)
+
+        def vf():
+            prefill_varlen(vqd, vkd, vvd, cqd, ckd, mq, causal=causal, window_left=window, scale=vscale, out=vod,
+                           lse=vld)
+        warm(vf, args.warmup)
+        st = stats(time_calls(vf, stream, legs_steps))
+        flops = 4 * 128 * hq * varlen_pairs(lens, causal, window)
+        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
+        result[name] = dict(config={"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128,
+                                    "causal": causal, "window_left": window}, **st, tflops=tf,
+                            flops_per_launch=flops,
+                            roofline=mfma_roofline("prefill_bf16_kernel<128, causal, varlen>", tf,
+                                                   name.replace("prefill_", "prefill_bf16_") + "_counters"))
+        del vqd, vkd, vvd, vod, vld
+        torch.cuda.empty_cache()
+        if result["value"] is None:
+            result["value"] = tf
+
+    if leg("backward"):
+        # backward of the MHA 4K causal workload: the forward's o and lse feed it
+        bc = I.PREFILL_MHA_4K
+        bq, bk, bv, bdo, bscale = I.backward_inputs(bc.B, bc.Hq, bc.Hkv, bc.N, bc.d, seed=1)
+        bqd, bkd, bvd, bdod = bq.to(dev), bk.to(dev), bv.to(dev), bdo.to(dev)
+        bo, blse = prefill(bqd, bkd, bvd, causal=True, scale=bscale)
+        bdq, bdk, bdv = torch.empty_like(bqd), torch.empty_like(bkd), torch.empty_like(bvd)
+        bws = torch.empty(prefill_backward_workspace_bytes(bc.B, bc.Hq, bc.N), dtype=torch.uint8, device=dev)
+
+        def bwf():
+            prefill_backward(bqd, bkd, bvd, bo, bdod, blse, causal=True, scale=bscale, dq=bdq, dk=bdk, dv=bdv,
+                             workspace=bws)
+        warm(bwf, args.warmup)
+        st = stats(time_calls(bwf, stream, legs_steps))
+        flops = 2.5 * prefill_flops(bc.B, bc.Hq, bc.N, bc.d, True)
+        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
+        result["backward"] = dict(config={"workload": bc.name, "flops": "2.5 x forward (five matrix products per "
+                                                                        "score)",
+                                          "kernels": "dQ (with the D and lse rows) + dK/dV"}, **st, tflops=tf,
+                                  flops_per_launch=flops,
+                                  roofline=mfma_roofline("bwd_dq_kernel + bwd_dkdv_kernel", tf, "backward_counters",
+                                                         src=BACKWARD_SRC))
+        if result["value"] is None:
+            result["value"] = tf
+
+    # ------------------------------------------------ the step (timed last): 128K prefill + decode
+    if run_p:
+        host["c5"], pf, pod, pld, p_mem = prefill_setup(pc)
     if run_d:
         ws = torch.empty(decode_workspace_bytes(dc.B, dc.Hq, dc.Hkv, dc.maxlen, dc.d), dtype=torch.uint8,
                          device=dev)
@@ -450,107 +562,6 @@ def main():
         if run_p:
             del pf
             torch.cuda.empty_cache()
-
-    # ------------------------------------------------ legs
-    legs_steps = max(1, K)
-    for name, cfg, counters, steps in (("prefill_mha_4k", I.PREFILL_MHA_4K, "prefill_bf16_mha4k_counters", legs_steps),
-                                       ("prefill_gqa_16k", I.PREFILL_GQA_16K, "prefill_bf16_gqa16k_counters",
-                                        max(1, min(K, 10)))):
-        if not leg(name):
-            continue
-        host[name], fn, od, ld, mem = prefill_setup(cfg)
-        for _ in range(min(args.warmup, 2)):
-            fn()
-        result[name] = prefill_record(cfg, time_calls(fn, stream, steps), mem, counters)
-        host[name + "_out"] = (od.cpu(), ld.cpu())
-        del fn, od, ld
-        torch.cuda.empty_cache()
-        if result["value"] is None:
-            result["value"] = result[name]["tflops"]
-
-    if leg("decode_paged"):
-        kpd, vpd, table, _ = I.paged_cache(dkd, dvd, dl, args.page_size, seed=11)
-        tbd = table.to(dev)
-        del dkd, dvd
-        pws = torch.empty(decode_paged_workspace_bytes(dc.B, dc.Hq, dc.Hkv, args.page_size, table.shape[1], dc.d),
-                          dtype=torch.uint8, device=dev)
-        pgo = torch.empty_like(dqd)
-
-        def pgf():
-            decode_paged(dqd, kpd, vpd, tbd, dld, scale=dscale, out=pgo, workspace=pws)
-        for _ in range(args.warmup):
-            pgf()
-        st = stats(time_calls(pgf, stream, legs_steps))
-        nbytes = decode_bytes(lens_host, dc.Hq, dc.Hkv, dc.d) + table.numel() * 4
-        gbs = nbytes / (st["ms_avg"] * 1e-3) / 1e9
-        result["decode_paged"] = dict(workload=dc.name + f"-paged{args.page_size}", page_size=args.page_size, **st,
-                                      GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS, bytes_per_launch=nbytes,
-                                      tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
-                                      roofline={"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
-                                                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                                "frac": gbs / PEAK_HBM_GBS,
-                                                "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)})
-        del kpd, vpd, pws
-        torch.cuda.empty_cache()
-        if result["value"] is None:
-            result["value"], result["unit"] = gbs, "GB/s"
-
-    # packed variable-length legs: a 4096-query chunk against a 16384-key prefix
-    # (GQA B2 Hq32 Hkv8 d128, causal bottom-right), and the MHA 4K workload
-    # with a 1024-key causal window
-    for name, lens, hq, hkv, causal, window in (("prefill_chunked", [(4096, 16384)] * 2, 32, 8, True, -1),
-                                                ("prefill_window", [(4096, 4096)] * 4, 32, 32, True, 1024)):
-        if not leg(name):
-            continue
-        vq, vk, vv, cq, ck, vscale = I.varlen_inputs(lens, hq, hkv, 128, seed=5)
-        vqd, vkd, vvd, cqd, ckd = vq.to(dev), vk.to(dev), vv.to(dev), cq.to(dev), ck.to(dev)
-        vod = torch.empty_like(vqd)
-        vld = torch.empty((hq, vq.shape[0]), dtype=torch.float32, device=dev)
-        mq = max(nq for nq, _ in lens)
-
-        def vf():
-            prefill_varlen(vqd, vkd, vvd, cqd, ckd, mq, causal=causal, window_left=window, scale=vscale, out=vod,
-                           lse=vld)
-        for _ in range(args.warmup):
-            vf()
-        st = stats(time_calls(vf, stream, legs_steps))
-        flops = 4 * 128 * hq * varlen_pairs(lens, causal, window)
-        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
-        result[name] = dict(config={"sequences": [list(x) for x in lens], "Hq": hq, "Hkv": hkv, "d": 128,
-                                    "causal": causal, "window_left": window}, **st, tflops=tf,
-                            flops_per_launch=flops,
-                            roofline=mfma_roofline("prefill_bf16_kernel<128, causal, varlen>", tf,
-                                                   name.replace("prefill_", "prefill_bf16_") + "_counters"))
-        del vqd, vkd, vvd, vod, vld
-        torch.cuda.empty_cache()
-        if result["value"] is None:
-            result["value"] = tf
-
-    if leg("backward"):
-        # backward of the MHA 4K causal workload: the forward's o and lse feed it
-        bc = I.PREFILL_MHA_4K
-        bq, bk, bv, bdo, bscale = I.backward_inputs(bc.B, bc.Hq, bc.Hkv, bc.N, bc.d, seed=1)
-        bqd, bkd, bvd, bdod = bq.to(dev), bk.to(dev), bv.to(dev), bdo.to(dev)
-        bo, blse = prefill(bqd, bkd, bvd, causal=True, scale=bscale)
-        bdq, bdk, bdv = torch.empty_like(bqd), torch.empty_like(bkd), torch.empty_like(bvd)
-        bws = torch.empty(prefill_backward_workspace_bytes(bc.B, bc.Hq, bc.N), dtype=torch.uint8, device=dev)
-
-        def bwf():
-            prefill_backward(bqd, bkd, bvd, bo, bdod, blse, causal=True, scale=bscale, dq=bdq, dk=bdk, dv=bdv,
-                             workspace=bws)
-        for _ in range(args.warmup):
-            bwf()
-        st = stats(time_calls(bwf, stream, legs_steps))
-        flops = 2.5 * prefill_flops(bc.B, bc.Hq, bc.N, bc.d, True)
-        tf = flops / (st["ms_avg"] * 1e-3) / 1e12
-        result["backward"] = dict(config={"workload": bc.name, "flops": "2.5 x forward (five matrix products per "
-                                                                        "score)",
-                                          "kernels": "dQ (with the D and lse rows) + dK/dV"}, **st, tflops=tf,
-                                  flops_per_launch=flops,
-                                  roofline=mfma_roofline("bwd_dq_kernel + bwd_dkdv_kernel", tf, "backward_counters",
-                                                         src=BACKWARD_SRC))
-        if result["value"] is None:
-            result["value"] = tf
 
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,

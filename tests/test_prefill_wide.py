@@ -80,3 +80,22 @@ def test_wide_varlen_single_sequence_equals_dense(causal, n):
     torch.cuda.synchronize()
     assert torch.equal(o.cpu(), od.cpu()[0].transpose(0, 1))
     assert torch.equal(lse.cpu(), ld.cpu()[0])
+
+
+def test_wide_varlen_128k_sequence_equals_dense():
+    """The 131072-token causal GQA workload (Hq64 Hkv8 d128) as one packed
+    sequence: its packed Q/O rows span 2 GiB, so row offsets pass 2^31 bytes.
+    Packed and dense prefill must agree bit for bit."""
+    print("wide varlen 128K single sequence", flush=True)
+    cfg = I.PREFILL_GQA_128K
+    q, k, v, scale = I.prefill_config_inputs(cfg)
+    qd, kd, vd = to_dev(q, k, v)
+    del q, k, v
+    od, ld = prefill(qd, kd, vd, causal=True, scale=scale)
+    qp, kp, vp = (x[0].transpose(0, 1).contiguous() for x in (qd, kd, vd))  # [n, H, d] on the device
+    del qd, kd, vd
+    cu = torch.tensor([0, cfg.N], dtype=torch.int32, device="cuda")
+    o, lse = prefill_varlen(qp, kp, vp, cu, cu, cfg.N, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, od[0].transpose(0, 1))
+    assert torch.equal(lse, ld[0])

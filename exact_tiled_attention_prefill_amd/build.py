@@ -1,7 +1,10 @@
 """Build libfa.so (the HIP kernels and the C ABI of include/fa.h) for gfx950.
 
 Each .hip source is compiled to an object with hipcc (in parallel), then
-linked into exact_tiled_attention_prefill_amd/libfa.so.  The hardware-ceiling
+linked into exact_tiled_attention_prefill_amd/libfa.so.  The device assembly
+of every library source is generated as well and checked for hazards the
+compiler does not guard around the kernels' inline-asm LDS copies
+(isa_check.py); a violation fails the build.  The hardware-ceiling
 probes the benchmark reports beside the nominal peaks are linked separately
 into libfa_probes.so (not part of the attention ABI).  Intermediate objects
 go to _build/ at the repository root.  Run `python -m
@@ -13,6 +16,11 @@ import os
 import shutil
 import subprocess
 import sys
+
+try:
+    from . import isa_check
+except ImportError:  # run as a script
+    import isa_check
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -62,6 +70,30 @@ def _compile(src, extra):
     return obj, r.stderr
 
 
+def _device_asm(src, extra):
+    """The device assembly hipcc generates for src with the same flags."""
+    out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
+def check_device_code(srcs=None, extra=()):
+    """Generate each source's device assembly and raise if isa_check finds a hazard."""
+    srcs = SOURCES if srcs is None else srcs
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        asms = dict(zip(srcs, ex.map(lambda s: _device_asm(s, list(extra)), srcs)))
+    bad = []
+    for src, asm in asms.items():
+        bad += [f"{src}: {fn}: {insn}: {rule}" for fn, insn, rule in isa_check.check_asm(asm)]
+    if bad:
+        raise RuntimeError("device code hazard around an inline-asm LDS copy:\n" + "\n".join(bad[:20]))
+
+
 def _link(objs, lib):
     tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
@@ -81,6 +113,7 @@ def build(verbose=False, extra_flags=()):
         for _, err in results.values():
             if err.strip():
                 print(err, file=sys.stderr)
+    check_device_code(SOURCES, extra_flags)
     _link([results[s][0] for s in SOURCES], LIB)
     _link([results[s][0] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB

@@ -71,10 +71,14 @@ __device__ __forceinline__ void bbarrier() {
   asm volatile("" ::: "memory");
 }
 // lane l's 16 bytes from base + off land at lds_wave_base + 16*l (inline asm:
-// not tracked by the compiler; completion is ordered by vmcnt + barrier)
+// not tracked by the compiler; completion is ordered by vmcnt + barrier).
+// The compiler applies no hazard rule to inline asm: s_nop 0 gives the m0
+// write just before the copy its one wait state, and the build checks the
+// generated code for a VALU write of the base SGPRs fewer than 5 wait
+// states before a copy (isa_check.py).
 __device__ __forceinline__ void bdma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
-  asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
 // A wave-uniform pointer forced into scalar registers (the copy takes its
 // base address from SGPRs).

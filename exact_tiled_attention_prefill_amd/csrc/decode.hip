@@ -412,15 +412,19 @@ __device__ __forceinline__ void dec_wait_vmem_le() {
 // lane l's 16 bytes from base + off land at lds_wave_base + 16*l (inline asm:
 // the compiler does not track it; completion is ordered by vmcnt + barrier).
 // The copies carry the non-temporal hint (nt): the cache is read once.
+// The compiler applies no hazard rule to inline asm: s_nop 0 gives the m0
+// write just before the copy its one wait state, and the build checks the
+// generated code for a VALU write of the base SGPRs fewer than 5 wait
+// states before a copy (isa_check.py).
 __device__ __forceinline__ void dec_dma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
-  asm volatile("global_load_lds_dwordx4 %0, %2 nt" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 nt" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
 // the same copy from a per-lane 64-bit address (paged caches: the rows of one
 // stage may come from different pages)
 __device__ __forceinline__ void dec_dma16_addr(const void* addr, uint8_t* lds_wave_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
-  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(addr), "{m0}"(m0) : "memory");
 }
 // Longest bf16 chunk (keys), and the most pool pages one chunk touches: its
 // keys over pages of >= 16 keys, plus one page for a chunk that does not start

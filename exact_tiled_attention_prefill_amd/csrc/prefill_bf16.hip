@@ -128,9 +128,13 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* lds_byte_ptr) {
 // tracking would otherwise wait for every in-flight ring tile before each LDS
 // read); completion is ordered explicitly by wait_vmem_le() and the ring
 // barrier.  The asm has no register outputs.
+// The compiler applies no hazard rule to inline asm: s_nop 0 gives the m0
+// write just before the copy its one wait state, and the build checks the
+// generated code for a VALU write of the base SGPRs fewer than 5 wait
+// states before a copy (isa_check.py).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint8_t* lds_wave_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_wave_base;
-  asm volatile("global_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(off), "{m0}"(m0), "s"(base) : "memory");
 }
 
 // VARLEN: packed variable-length sequences (VarlenRef); N is then the longest

@@ -159,11 +159,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   // ordering is explicit (vmcnt + lgkmcnt + barrier).
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int x = lane & 31;
-  const int hi = lane >> 5;
+  const int wave = (int)threadIdx.x >> 6;
 
   // ---- work item: XCD-contiguous ranges of (block of KV groups, slot, group
   // in the block, head).  A block holds at least block_heads query heads so
@@ -221,19 +217,28 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   if (CAUSAL && (tslot > n_qt - 1 - tslot || (pass == 1 && tslot == n_qt - 1 - tslot))) continue;
   if (VARLEN && !CAUSAL && tslot >= n_qt) continue;
 
+  // Every lane-dependent value of the pass derives from the lane id taken
+  // here (mbcnt, in volatile asm so that it is not hoisted), so the compiler
+  // recomputes such values per pass instead of keeping them live (and
+  // spilled) across the pass loop.
+  int lp;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lp));
+  const int xp = lp & 31, hp = lp >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar: LDS bases go to M0 directly
+
   // Rows of this wave: q0 + wave + kWaves*j; lane column x holds row q0 + wave + kWaves*x.
   const int q0 = qtile * kBR;
-  const int qrow = q0 + wave + kWaves * x;
-  const int wave_first = q0 + wave;
+  const int qrow = q0 + wave_s + kWaves * xp;
+  const int wave_first = q0 + wave_s;
   const bool wave_has_rows = wave_first < Lq;
-  const int wave_last_row = min(q0 + wave + kWaves * 31, Lq - 1);
+  const int wave_last_row = min(q0 + wave_s + kWaves * 31, Lq - 1);
 
   // Q fragments (B operand of S^T = K Q^T): column x, d = 16ks + 8hi + 0..7.
   // All loads are issued before any is used (rows past the end read the last
   // row and are zeroed afterwards).
   bf16x8 qf[KS];
   {
-    const uint16_t* qr = qh + (size_t)min(qrow, Lq - 1) * q_rs + hi * 8;
+    const uint16_t* qr = qh + (size_t)min(qrow, Lq - 1) * q_rs + hp * 8;
     u32x4 w[KS];
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) w[kq] = *reinterpret_cast<const u32x4*>(qr + kq * 16);
@@ -243,12 +248,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   }
 
   // ---- per-lane LDS read offsets (tile base and ks/mb/ks2 parts are immediates) ----
-  // They are derived from a copy of the lane id taken inside the pass, so the
-  // compiler recomputes them per pass instead of keeping them live (and
-  // spilled) across the whole kernel.
-  int lp;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(lp) : "v"(lane));
-  const int xp = lp & 31, hp = lp >> 5;
   int koff[KS];  // K: row x (+32 mb), chunk (2ks + hi) swizzled
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = xp * (D * 2) + (((2 * ks + hp) ^ k_swz<D>(xp)) << 4);
@@ -263,12 +262,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   }
 
   // ---- DMA: chunk p = i*kThreads + wave*64 + lane of the tile; byte offsets within the tile ----
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar: LDS bases go to M0 directly
   // rows of chunk i are dma_row + i*kRowStep; the swizzle depends on the row
   // only modulo 16, so one offset serves every chunk of a lane
   constexpr int kRowStep = kThreads / RC;
   static_assert(kRowStep % 16 == 0, "row step keeps the swizzle");
-  const int dma_row = (wave * 64 + lp) / RC;
+  const int dma_row = (wave_s * 64 + lp) / RC;
   const int dma_cp = lp % RC;
   const uint32_t dk_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ k_swz<D>(dma_row)) << 4));
   const uint32_t dv_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ v_swz<D>(dma_row)) << 4));
@@ -314,9 +312,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   };
   // key = k0 + 4hi + o, o = 32mb + 8(r/4) + r%4: masked when o > lim (or o < lim_lo)
   auto mask_scores = [&](f32x16 (&s)[kMB], int k0) {
-    const int lim = (CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1) - k0 - 4 * hi;
+    const int lim = (CAUSAL ? min(qrow + off, Lk - 1) : Lk - 1) - k0 - 4 * hp;
     if (W >= 0) {
-      const int lim_lo = qrow + off - W - k0 - 4 * hi;
+      const int lim_lo = qrow + off - W - k0 - 4 * hp;
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -488,29 +486,35 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 
   // ---- epilogue: O = O^T / l, lse = m ln2 + ln l ----
   if (wave_has_rows) {
+  // the row and the output addresses come from the lane id taken afresh, so
+  // that no 64-bit address stays live (and spilled) through the tile loop
+  int le;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+  const int row_e = q0 + wave_s + kWaves * (le & 31);
+  const int he = le >> 5;
   const float lt = sum_halves(l_run);
   // a packed causal row with i + off < 0 (or a sequence without keys) sees no
   // key: o = 0, lse = -inf, decided by position, not by arithmetic
-  const bool empty = VARLEN && ((CAUSAL && qrow + off < 0) || Lk == 0);
+  const bool empty = VARLEN && ((CAUSAL && row_e + off < 0) || Lk == 0);
   const float inv = empty ? 0.f : 1.0f / lt;
-  if (qrow < Lq) {
-    uint16_t* orow = o + qbase + (size_t)qrow * q_rs;
+  if (row_e < Lq) {
+    uint16_t* orow = o + qbase + (size_t)row_e * q_rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = md * 32 + 8 * g4 + 4 * hi;
+        const int d0 = md * 32 + 8 * g4 + 4 * he;
         u32x2 w = {pack_bf16x2(oacc[md][4 * g4 + 0] * inv, oacc[md][4 * g4 + 1] * inv),
                    pack_bf16x2(oacc[md][4 * g4 + 2] * inv, oacc[md][4 * g4 + 3] * inv)};
         if (empty) w = u32x2{0u, 0u};
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-    if (lse != nullptr && hi == 0) {
+    if (lse != nullptr && he == 0) {
       const float lv = empty ? -INFINITY : m_run * kLn2 + __logf(lt);
       if (VARLEN)
-        lse[(size_t)h * vr.total_q + qstart + qrow] = lv;
+        lse[(size_t)h * vr.total_q + qstart + row_e] = lv;
       else
-        lse[(size_t)bh * N + qrow] = lv;
+        lse[(size_t)bh * N + row_e] = lv;
     }
   }
   }  // wave_has_rows

@@ -341,12 +341,12 @@ __global__ __launch_bounds__(kBThreads, 2) void bwd_dq_kernel(
   issue(0, ring[0][0], ring[0][1]);
   bwait_vmem_le<0>();
   bbarrier();
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  // unrolled by two; an odd last tile is the loop's skipped second half (a
+  // workgroup-uniform branch), so there is no separate tail copy of the step
+  for (int t = 0; t < ntiles; t += 2) {
     step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
   }
-  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
   if (wave_has_rows && qrow < N) {
     uint16_t* orow = dq + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -626,34 +626,42 @@ __global__ __launch_bounds__(kBKThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int t = 0; t < KS; ++t) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, kf[t])));
   bbarrier();
-  int u = 0;
-  for (; u + 1 < total; u += 2) {
+  // unrolled by two; an odd last step is the loop's skipped second half
+  // (a workgroup-uniform branch), so no separate tail copy of the step keeps
+  // its per-lane offsets live (and spilled) past the loop
+  for (int u = 0; u < total; u += 2) {
     step(u, std::integral_constant<int, 0>{});
-    step(u + 1, std::integral_constant<int, 1>{});
+    if (u + 1 < total) step(u + 1, std::integral_constant<int, 1>{});
   }
-  if (u < total) step(u, std::integral_constant<int, 0>{});
 
   // Sum the two halves through LDS (every wave is past the last barrier, no
   // copy is in flight), then the lower waves store.  Register r of block md
-  // holds key k0b + 32kw + 8(r/4) + 4hi + r%4 and column d = 32md + x.
+  // holds key k0b + 32kw + 8(r/4) + 4hi + r%4 and column d = 32md + x.  The
+  // lane id is taken afresh (mbcnt, in volatile asm so that it is not
+  // hoisted) and the wave split comes from the scalar wave index, so no
+  // per-lane epilogue address stays live (and spilled) through the loop.
+  int le;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+  const int xe = le & 31, he = le >> 5;
+  const int kw_e = wave_s & 3, half_e = wave_s >> 2;
   float* red = reinterpret_cast<float*>(&ring[0][0][0]);
-  auto red_idx = [&](int md, int r) { return (kw * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * D + 32 * md + x; };
+  auto red_idx = [&](int md, int r) { return (kw_e * 32 + 8 * (r >> 2) + 4 * he + (r & 3)) * D + 32 * md + xe; };
   auto reduce_store = [&](f32x16(&acc)[MD], uint16_t* out, float mul) {
-    if (half == 1) {
+    if (half_e == 1) {
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[red_idx(md, r)] = acc[md][r];
     }
     __syncthreads();
-    if (half == 0) {
+    if (half_e == 0) {
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = k0b + 32 * kw + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int kk = k0b + 32 * kw_e + 8 * (r >> 2) + 4 * he + (r & 3);
           const float val = (acc[md][r] + red[red_idx(md, r)]) * mul;
-          if (kk < N) out[kvbase + (size_t)kk * D + 32 * md + x] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
+          if (kk < N) out[kvbase + (size_t)kk * D + 32 * md + xe] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xffffu);
         }
     }
     __syncthreads();

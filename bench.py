@@ -47,6 +47,8 @@ PREFILL_SRC = os.path.join(CSRC, "prefill_bf16.hip")
 DECODE_SRC = os.path.join(CSRC, "decode.hip")
 BACKWARD_SRC = os.path.join(CSRC, "backward_bf16.hip")
 BAR = {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3}
+# backward: the forward's bf16 bar scaled to each gradient's range s = max(1, max|ref|)
+BWD_BAR = {"max_abs_over_range": 2e-2, "mean_abs_over_range": 2e-3}
 PREFILL_KERNEL = "prefill_bf16_kernel<128, causal> (4 or 8 waves per workgroup, as the launcher picks)"
 
 
@@ -209,6 +211,46 @@ def _oracle_job(job):
         emax, esum, count, lmax = max(emax, float(e.max())), esum + float(e.sum()), count + e.size, max(
             lmax, float(el.max()))
     return flops, emax, esum, count, lmax
+
+
+def _oracle_bwd_job(job):
+    """One head's dq, dk, dv through the fp64 oracle's backward (run in a pool
+    worker) and the GPU gradients' errors, each over the gradient's range
+    s = max(1, max|ref|).  Tensors arrive as raw bf16 bits (uint16)."""
+    import numpy as np
+
+    import oracle
+
+    qh, kh, vh, doh, grads, scale = job
+    bf16 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)[None, None]  # exact bf16 -> fp32
+    refs = oracle.attention_backward(bf16(qh), bf16(kh), bf16(vh), bf16(doh), True, scale)
+    out = []
+    for g, r in zip(grads, refs):
+        e = np.abs(bf16(g).astype(np.float64) - r)
+        s = max(1.0, float(np.abs(r).max()))
+        out.append((float(e.max()) / s, float(e.mean()) / s))
+    return out
+
+
+def oracle_backward_check(pool, q, k, v, do, scale, grads_gpu):
+    """Compare the GPU backward of every (batch, head) of an MHA causal
+    workload with the oracle.  Returns the worst ratios per gradient."""
+    import torch
+
+    B, Hq = q.shape[:2]
+    assert k.shape[1] == Hq, "one head per job needs MHA (each head's gradients depend on it alone)"
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view("uint16")
+    jobs = ((bits(q[b, h]), bits(k[b, h]), bits(v[b, h]), bits(do[b, h]), [bits(g[b, h]) for g in grads_gpu],
+             scale) for b in range(B) for h in range(Hq))
+    t0 = time.perf_counter()
+    res = list(pool.imap_unordered(_oracle_bwd_job, jobs, chunksize=1))
+    dt = time.perf_counter() - t0
+    err = {}
+    for i, name in enumerate(("dq", "dk", "dv")):
+        err[name] = {"max_abs_over_range": max(r[i][0] for r in res),
+                     "mean_abs_over_range": max(r[i][1] for r in res)}
+    err["within_bar"] = all(err[n][key] <= BWD_BAR[key] for n in ("dq", "dk", "dv") for key in BWD_BAR)
+    return err, dt
 
 
 def oracle_check(pool, q, k, v, scale, o_gpu, lse_gpu, rows, heads_per_job):
@@ -500,6 +542,11 @@ def main():
                                                          src=BACKWARD_SRC))
         if result["value"] is None:
             result["value"] = tf
+        if pool is not None:
+            host["backward"] = (bq, bk, bv, bdo, bscale)
+            host["backward_out"] = (bdq.cpu(), bdk.cpu(), bdv.cpu())
+        del bqd, bkd, bvd, bdod, bo, blse, bdq, bdk, bdv, bws
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------ the step (timed last): 128K prefill + decode
     if run_p:
@@ -601,6 +648,12 @@ def main():
                                           heads_per_job=1)
             parity[cfg.name] = dict(rows=f"all {cfg.N} rows x {cfg.B * cfg.Hq} heads", bar=BAR, oracle_seconds=dt,
                                     **err)
+        if "backward_out" in host:
+            bq, bk, bv, bdo, bscale = host["backward"]
+            err, dt = oracle_backward_check(pool, bq, bk, bv, bdo, bscale, host["backward_out"])
+            bc = I.PREFILL_MHA_4K
+            parity["backward " + bc.name] = dict(heads=f"dq, dk, dv of all {bc.B * bc.Hq} heads", bar=BWD_BAR,
+                                                 oracle_seconds=dt, **err)
         pool.close()
         pool.join()
         result["parity"] = parity

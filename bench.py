@@ -232,6 +232,109 @@ def _oracle_bwd_job(job):
     return out
 
 
+def _oracle_varlen_job(job):
+    """One packed sequence and query head through the fp64 oracle's
+    attention_varlen (run in a pool worker), and the GPU output's error on its
+    rows.  Tensors arrive as raw bf16 bits (uint16), lse as float32."""
+    import numpy as np
+
+    import oracle
+
+    qh, kh, vh, causal, window, oh, lh, scale = job
+    bf16 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)  # exact bf16 -> fp32
+    n_q, n_k = qh.shape[0], kh.shape[0]
+    ro, rl = oracle.attention_varlen(bf16(qh)[:, None], bf16(kh)[:, None], bf16(vh)[:, None], [0, n_q], [0, n_k],
+                                     causal, scale, window_left=window)
+    e = np.abs(bf16(oh).astype(np.float64) - ro[:, 0])
+    el = np.abs(lh.astype(np.float64) - rl[0])
+    return float(e.max()), float(e.sum()), e.size, float(el.max())
+
+
+def oracle_varlen_check(pool, q, k, v, cu_q, cu_k, causal, window, scale, o_gpu, lse_gpu):
+    """Compare every row of every head of a packed prefill with the oracle,
+    one (sequence, head) per job."""
+    import torch
+
+    hq, hkv = q.shape[1], k.shape[1]
+    G = hq // hkv
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view("uint16")
+    cq, ck = cu_q.tolist(), cu_k.tolist()
+
+    def jobs():
+        for b in range(len(cq) - 1):
+            for h in range(hq):
+                yield (bits(q[cq[b]:cq[b + 1], h]), bits(k[ck[b]:ck[b + 1], h // G]),
+                       bits(v[ck[b]:ck[b + 1], h // G]), causal, window, bits(o_gpu[cq[b]:cq[b + 1], h]),
+                       lse_gpu[h, cq[b]:cq[b + 1]].numpy(), scale)
+
+    t0 = time.perf_counter()
+    res = list(pool.imap_unordered(_oracle_varlen_job, jobs(), chunksize=1))
+    dt = time.perf_counter() - t0
+    count = sum(r[2] for r in res)
+    err = {"o_max_abs": max(r[0] for r in res), "o_mean_abs": sum(r[1] for r in res) / count,
+           "lse_max_abs": max(r[3] for r in res)}
+    err["within_bar"] = all(err[key] <= BAR[key] for key in BAR)
+    return err, dt
+
+
+def _oracle_decode_job(job):
+    """One decode sequence (all query heads) through the fp64 oracle (run in a
+    pool worker), and the errors of the GPU outputs given for it."""
+    import numpy as np
+
+    import oracle
+
+    qb, kb, vb, n, outs, scale = job
+    bf16 = lambda a: (a.astype(np.uint32) << 16).view(np.float32)  # exact bf16 -> fp32
+    ro, _ = oracle.decode(bf16(qb)[None], bf16(kb)[None], bf16(vb)[None], np.array([n]), scale)
+    res = []
+    for ob in outs:
+        e = np.abs(bf16(ob).astype(np.float64) - ro[0])
+        res.append((float(e.max()), float(e.sum()), e.size))
+    return res
+
+
+def oracle_decode_check(pool, q, kcache_dev, vcache_dev, lens, scale, outs, seqs):
+    """Compare the GPU decode outputs `outs` (name -> [B,Hq,d] host tensor) on
+    the sequences `seqs` with the oracle; the cache rows of each sequence are
+    copied from the device as its job is made."""
+    import torch
+
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view("uint16")
+    names = list(outs)
+
+    def jobs():
+        for b in seqs:
+            n = int(lens[b])
+            yield (bits(q[b]), bits(kcache_dev[b, :, :n].cpu()), bits(vcache_dev[b, :, :n].cpu()), n,
+                   [bits(outs[name][b]) for name in names], scale)
+
+    t0 = time.perf_counter()
+    res = list(pool.imap_unordered(_oracle_decode_job, jobs(), chunksize=1))
+    dt = time.perf_counter() - t0
+    out = {}
+    for i, name in enumerate(names):
+        count = sum(r[i][2] for r in res)
+        err = {"o_max_abs": max(r[i][0] for r in res), "o_mean_abs": sum(r[i][1] for r in res) / count}
+        err["within_bar"] = err["o_max_abs"] <= BAR["o_max_abs"] and err["o_mean_abs"] <= BAR["o_mean_abs"]
+        out[name] = err
+    return out, dt
+
+
+def decode_sample_sequences(lens, count=16, seed=4):
+    """The two shortest and two longest decode sequences and seeded others, `count` in all."""
+    import torch
+
+    order = sorted(range(len(lens)), key=lambda b: lens[b])
+    seqs = set(order[:2] + order[-2:])
+    gen = torch.Generator().manual_seed(seed)
+    for b in torch.randperm(len(lens), generator=gen).tolist():
+        if len(seqs) >= min(count, len(lens)):
+            break
+        seqs.add(b)
+    return sorted(seqs)
+
+
 def oracle_backward_check(pool, q, k, v, do, scale, grads_gpu):
     """Compare the GPU backward of every (batch, head) of an MHA causal
     workload with the oracle.  Returns the worst ratios per gradient."""
@@ -483,6 +586,8 @@ def main():
                                                 "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                                 "frac": gbs / PEAK_HBM_GBS,
                                                 "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)})
+        if pool is not None:
+            host["decode_paged_out"] = pgo.cpu()
         del kpd, vpd, pws
         torch.cuda.empty_cache()
         if result["value"] is None:
@@ -513,6 +618,9 @@ def main():
                             flops_per_launch=flops,
                             roofline=mfma_roofline("prefill_bf16_kernel<128, causal, varlen>", tf,
                                                    name.replace("prefill_", "prefill_bf16_") + "_counters"))
+        if pool is not None:
+            host[name] = (vq, vk, vv, cq, ck, causal, window, vscale)
+            host[name + "_out"] = (vod.cpu(), vld.cpu())
         del vqd, vkd, vvd, vod, vld
         torch.cuda.empty_cache()
         if result["value"] is None:
@@ -606,6 +714,8 @@ def main():
                                                                             "shader_clock_ghz"))})
             if result["value"] is None:
                 result["value"], result["unit"] = gbs, "GB/s"
+            if pool is not None:
+                host["decode_out"] = dod.cpu()
         if run_p:
             del pf
             torch.cuda.empty_cache()
@@ -648,6 +758,22 @@ def main():
                                           heads_per_job=1)
             parity[cfg.name] = dict(rows=f"all {cfg.N} rows x {cfg.B * cfg.Hq} heads", bar=BAR, oracle_seconds=dt,
                                     **err)
+        for name in ("prefill_chunked", "prefill_window"):
+            if name + "_out" not in host:
+                continue
+            vq, vk, vv, cq, ck, causal, window, vscale = host[name]
+            err, dt = oracle_varlen_check(pool, vq, vk, vv, cq, ck, causal, window, vscale, *host[name + "_out"])
+            parity[name] = dict(rows=f"all {vq.shape[0]} packed rows x {vq.shape[1]} heads", bar=BAR,
+                                oracle_seconds=dt, **err)
+        outs = {k_: host[k_ + "_out"] for k_ in ("decode", "decode_paged") if k_ + "_out" in host}
+        if outs:
+            seqs = decode_sample_sequences(lens_host)
+            errs, dt = oracle_decode_check(pool, dq, dkd, dvd, lens_host, dscale, outs, seqs)
+            for k_, err in errs.items():
+                parity[k_ + " " + dc.name] = dict(sequences=f"{len(seqs)} of {dc.B} sequences (the 2 shortest, "
+                                                  f"the 2 longest, seeded others) x {dc.Hq} heads",
+                                                  bar={"o_max_abs": BAR["o_max_abs"], "o_mean_abs": BAR["o_mean_abs"]},
+                                                  oracle_seconds=dt, **err)
         if "backward_out" in host:
             bq, bk, bv, bdo, bscale = host["backward"]
             err, dt = oracle_backward_check(pool, bq, bk, bv, bdo, bscale, host["backward_out"])

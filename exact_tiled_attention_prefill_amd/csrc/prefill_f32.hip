@@ -8,8 +8,20 @@
 // During Local Inference?", "Kernel Fusion Keeps More of the Attention Chain
 // in One Execution Path").
 //
-// Layout: one thread per query row (q and the output accumulator in VGPRs),
-// 128 rows per workgroup, 32-key fp32 K/V tiles in LDS read as broadcasts.
+// Layout: one thread per query row, 128 rows per workgroup; the output
+// accumulator in registers, the rows' q in LDS (padded by one word, so the
+// 128 threads' reads of their own rows fall in different banks), 32-key fp32
+// K/V tiles in LDS read as broadcasts.
+//
+// Precision: fp32 inputs and outputs, fp64 sums.  The scores q.k, the
+// running max, the output accumulator and the running sum are fp64, and the
+// exponentials exp2f of the (fp64-formed) arguments are fp32.  In fp32 a row's
+// sum of N terms p * v grows a rounding error like sqrt(N) * 2^-24 * |o|
+// (about 1e-5 at N = 2800, |o| = 4), and the 128-term fp32 dot product puts
+// ~5e-6 (log2 units) into each exponent at |scale| = 0.45, which a sharp
+// softmax turns into ~1e-5 of output error; products of fp32 values are exact
+// in fp64.  What is left is the fp32 exponentials and the fp32 coefficient
+// c, about 1e-6 of the output and of lse.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,6 +36,7 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, int n_qtiles, int BH,
     float c, float qsign) {
+  __shared__ float qs[kF32Rows][D + 1];
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
   const int tid = threadIdx.x;
@@ -41,13 +54,18 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(
   const int row = q0 + tid;
   const bool live = row < N;
 
-  float qr[D], acc[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    qr[i] = live ? qsign * qh[(size_t)row * D + i] : 0.f;
-    acc[i] = 0.f;
+  double acc[D];
+  // q rows of the workgroup into LDS (coalesced: consecutive threads read
+  // consecutive elements)
+  for (int e = tid; e < kF32Rows * D; e += kF32Rows) {
+    const int r = e / D, cc = e % D;
+    qs[r][cc] = q0 + r < N ? qsign * qh[(size_t)(q0 + r) * D + cc] : 0.f;
   }
-  float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) acc[i] = 0.0;
+  const double cd = (double)c;
+  double m_run = -INFINITY;  // running max of c * (q . k), log2 units
+  double l_run = 0.0;
 
   const int kv_end = CAUSAL ? min(N, q0 + kF32Rows) : N;
   for (int k0 = 0; k0 < kv_end; k0 += kF32Keys) {
@@ -59,38 +77,43 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(
       vs[r][cc] = ok ? vh[(size_t)(k0 + r) * D + cc] : 0.f;
     }
     __syncthreads();
-    float s[kF32Keys];
-    float mx = -INFINITY;
+    // s[j] = q . k_j in fp64, summed over i in order
+    double s[kF32Keys];
+#pragma unroll
+    for (int j = 0; j < kF32Keys; ++j) s[j] = 0.0;
+    for (int i = 0; i < D; ++i) {
+      const double qi = (double)qs[tid][i];
+#pragma unroll
+      for (int j = 0; j < kF32Keys; ++j) s[j] = fma(qi, (double)ks[j][i], s[j]);
+    }
+    double mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < D; ++i) dot = fmaf(qr[i], ks[j][i], dot);
       const int key = k0 + j;
       const bool masked = key >= N || (CAUSAL && key > row);
-      s[j] = masked ? -INFINITY : dot;
-      mx = fmaxf(mx, s[j]);
+      s[j] = masked ? -INFINITY : s[j];
+      mx = fmax(mx, s[j]);
     }
-    const float mn = fmaxf(m_run, mx * c);
+    const double mn = fmax(m_run, mx * cd);
     if (mn == -INFINITY) continue;  // nothing visible yet (padding rows only)
-    const float alpha = fast_exp2(m_run - mn);
+    const double alpha = (double)exp2f((float)(m_run - mn));
     l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[i] *= alpha;
     m_run = mn;
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
-      const float p = exp2f(fmaf(s[j], c, -mn));
+      const double p = (double)exp2f((float)fma(s[j], cd, -mn));
       l_run += p;
 #pragma unroll
-      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, vs[j][i], acc[i]);
+      for (int i = 0; i < D; ++i) acc[i] = fma(p, (double)vs[j][i], acc[i]);
     }
   }
   if (!live) return;
-  const float inv = 1.0f / l_run;
+  const double inv = 1.0 / l_run;
 #pragma unroll
-  for (int i = 0; i < D; ++i) o[(size_t)bh * N * D + (size_t)row * D + i] = acc[i] * inv;
-  if (lse != nullptr) lse[(size_t)bh * N + row] = m_run * kLn2 + logf(l_run);
+  for (int i = 0; i < D; ++i) o[(size_t)bh * N * D + (size_t)row * D + i] = (float)(acc[i] * inv);
+  if (lse != nullptr) lse[(size_t)bh * N + row] = (float)(m_run * 0.6931471805599453 + log(l_run));
 }
 
 template <int D, bool CAUSAL>

@@ -4,8 +4,11 @@ The hand-picked cases elsewhere cover tile edges and the published
 workloads; these draw shapes, head groupings, masks, scales and (packed)
 sequence lengths from a fixed seed, so that combinations nobody picked by hand
 are compared element by element with the fp64 oracle too.  Each case prints
-its parameters before it runs.  Bars: bf16 max-abs 2e-2 and mean-abs 2e-3 on
-O, 1e-3 on lse; fp32 1e-5.
+its parameters before it runs.  The scales reach 5.7x the named workloads'
+1/sqrt(d), so the bf16 outputs are held to the per-element bar their
+arithmetic gives (gpu_util.check_bf16_elementwise: (2^-8 + 2^-10) (|o| + a) +
+1e-5 with a the oracle's output for |V|) and mean-abs 2e-3, lse to 1e-3;
+fp32 to 1e-5.
 """
 
 import random
@@ -17,7 +20,7 @@ import torch
 import oracle
 from exact_tiled_attention_prefill_amd import decode, prefill, prefill_varlen
 from exact_tiled_attention_prefill_amd import inputs as I
-from gpu_util import BF16_LSE_MAX_ABS, F32_LSE_MAX_ABS, F32_MAX_ABS, check_bf16, check_close, f64, to_dev
+from gpu_util import BF16_LSE_MAX_ABS, F32_LSE_MAX_ABS, F32_MAX_ABS, check_bf16_elementwise, check_close, f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +50,8 @@ def test_random_dense_prefill_bf16(B, Hkv, G, N, d, causal, scale, seed):
     o, lse = prefill(*to_dev(q, k, v), causal=causal, scale=scale)
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, causal, scale)
-    check_bf16(o, ro, "o")
+    ra, _ = oracle.attention(q, k, v.abs(), causal, scale)
+    check_bf16_elementwise(o, ro, ra, "o")
     check_close(lse, rl, BF16_LSE_MAX_ABS, "lse")
 
 
@@ -85,8 +89,9 @@ def test_random_wide_prefill_bf16(Hkv, G, N, causal, seed):
     rows = sorted({0, 1, 255, 256, N - 2, N - 1} | {rng.randrange(N) for _ in range(30)})
     heads = [(0, h) for h in range(Hkv * G)]
     ro, rl = oracle.attention_rows(q, k, v, causal, scale, rows, heads)
+    ra, _ = oracle.attention_rows(q, k, v.abs(), causal, scale, rows, heads)
     idx = torch.as_tensor(rows)
-    check_bf16(torch.stack([o[0, h][idx] for _, h in heads]), ro, "wide o")
+    check_bf16_elementwise(torch.stack([o[0, h][idx] for _, h in heads]), ro, ra, "wide o")
     check_close(torch.stack([lse[0, h][idx] for _, h in heads]), rl, BF16_LSE_MAX_ABS, "wide lse")
 
 
@@ -117,7 +122,8 @@ def test_random_varlen_prefill(lens, Hkv, G, d, causal, window, seed):
     o, lse = prefill_varlen(*to_dev(q, k, v, cu_q, cu_k), max_q, causal=causal, window_left=window, scale=scale)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=window)
-    check_bf16(o, ro, "varlen o")
+    ra, _ = oracle.attention_varlen(q, k, v.abs(), cu_q, cu_k, causal, scale, window_left=window)
+    check_bf16_elementwise(o, ro, ra, "varlen o")
     g = f64(lse)
     empty = np.isneginf(rl)
     assert np.array_equal(np.isneginf(g), empty), "rows without keys differ"
@@ -150,7 +156,8 @@ def test_random_decode(lens, maxlen, Hkv, G, d, dtype, seed):
     if dtype == "f32":
         check_close(o, ro, F32_MAX_ABS, "decode f32")
     else:
-        check_bf16(o, ro, "decode bf16")
+        ra, _ = oracle.decode(q, kc, vc.abs(), ls, scale)
+        check_bf16_elementwise(o, ro, ra, "decode bf16")
     for b, n in enumerate(lens):
         if n == 0:
             assert torch.all(o.cpu()[b] == 0)

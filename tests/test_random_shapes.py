@@ -1,8 +1,9 @@
 """GPU parity on seeded random shapes across the entry points.
 
 The hand-picked cases elsewhere cover tile edges and the published
-workloads; these draw shapes, head groupings, masks, scales and (packed)
-sequence lengths from a fixed seed, so that combinations nobody picked by hand
+workloads; these draw shapes, head groupings, masks, scales, (packed)
+sequence lengths and page sizes from a fixed seed, for every entry point
+including the backward and the paged decode, so that combinations nobody picked by hand
 are compared element by element with the fp64 oracle too.  Each case prints
 its parameters before it runs.  The scales reach 5.7x the named workloads'
 1/sqrt(d), so the bf16 outputs are held to the per-element bar their
@@ -18,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from exact_tiled_attention_prefill_amd import decode, prefill, prefill_varlen
+from exact_tiled_attention_prefill_amd import decode, decode_paged, prefill, prefill_backward, prefill_varlen
 from exact_tiled_attention_prefill_amd import inputs as I
 from gpu_util import BF16_LSE_MAX_ABS, F32_LSE_MAX_ABS, F32_MAX_ABS, check_bf16_elementwise, check_close, f64, to_dev
 
@@ -161,3 +162,59 @@ def test_random_decode(lens, maxlen, Hkv, G, d, dtype, seed):
     for b, n in enumerate(lens):
         if n == 0:
             assert torch.all(o.cpu()[b] == 0)
+
+
+def _backward_cases(n, seed):
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        d = rng.choice([64, 128])
+        hkv, g, b = rng.choice([1, 2]), rng.choice([1, 2, 3, 4]), rng.choice([1, 2])
+        nn = rng.choice([rng.randint(1, 80), rng.randint(80, 400), rng.randint(400, 700)])
+        out.append((b, hkv, g, nn, d, rng.random() < 0.6, rng.choice([None, rng.uniform(-0.3, 0.4)]),
+                    rng.randint(0, 10 ** 6)))
+    return out
+
+
+@pytest.mark.parametrize("B,Hkv,G,N,d,causal,scale,seed", _backward_cases(8, 4242))
+def test_random_backward(B, Hkv, G, N, d, causal, scale, seed):
+    """dq, dk, dv against the oracle's backward, with the bar of tests/test_backward.py."""
+    print(f"backward B{B} Hkv{Hkv} G{G} N{N} d{d} causal={causal} scale={scale}", flush=True)
+    q, k, v, do, s0 = I.backward_inputs(B, Hkv * G, Hkv, N, d, seed=seed)
+    scale = s0 if scale is None else scale
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = prefill(qd, kd, vd, causal=causal, scale=scale)
+    grads = prefill_backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for g, r, name in zip(grads, oracle.attention_backward(q, k, v, do, causal, scale), ("dq", "dk", "dv")):
+        err = np.abs(f64(g) - r)
+        s = max(1.0, float(np.abs(r).max()))
+        assert np.isfinite(err).all(), f"{name}: non-finite"
+        assert err.max() <= 2e-2 * s and err.mean() <= 2e-3 * s, (name, err.max(), err.mean(), s)
+
+
+def _paged_cases(n, seed):
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        maxlen = rng.choice([rng.randint(1, 300), rng.randint(300, 6000), rng.randint(6000, 20000)])
+        lens = [rng.randint(0, maxlen) for _ in range(rng.randint(1, 8))]
+        out.append((rng.choice([16, 32, 64, 128, 256, 512, 1024]), rng.choice([64, 128]), rng.choice([1, 2, 4]),
+                    rng.choice([1, 2, 4, 8, 16]), lens, maxlen, rng.randint(0, 10 ** 6)))
+    return out
+
+
+@pytest.mark.parametrize("page,d,Hkv,G,lens,maxlen,seed", _paged_cases(6, 5151))
+def test_random_paged_decode(page, d, Hkv, G, lens, maxlen, seed):
+    """Paged decode against the oracle, and bit-identical to contiguous decode of the same cache."""
+    print(f"paged decode page{page} d{d} Hkv{Hkv} G{G} B{len(lens)} maxlen{maxlen}", flush=True)
+    q, kc, vc, ls, scale = I.decode_inputs(len(lens), Hkv * G, Hkv, d, 0, maxlen, maxlen, "bf16", seed=seed,
+                                           seqlens=lens)
+    kp, vp, table, _ = I.paged_cache(kc, vc, ls, page, seed=seed)
+    o = decode_paged(*to_dev(q, kp, vp, table, ls), scale=scale)
+    oc = decode(*to_dev(q, kc, vc, ls), scale=scale)
+    torch.cuda.synchronize()
+    ro, _ = oracle.decode_paged(q, kp, vp, table, ls, scale)
+    ra, _ = oracle.decode_paged(q, kp, vp.abs(), table, ls, scale)
+    check_bf16_elementwise(o, ro, ra, "paged decode o")
+    assert torch.equal(o, oc), "paged and contiguous decode differ on the same logical cache"

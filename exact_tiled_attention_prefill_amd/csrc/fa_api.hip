@@ -65,6 +65,7 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, float* 
   st = check_device();
   if (st != FA_OK) return st;
   fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_coeff(scale), scale < 0.f};
+  a.scale_abs = std::fabs(scale);
   hipError_t e = bf16 ? fa::launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
                       : fa::launch_prefill_f32(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

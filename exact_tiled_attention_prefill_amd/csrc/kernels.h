@@ -41,6 +41,7 @@ struct PrefillArgs {
   float c;       // |scale| * log2(e), >= kMinC
   bool neg;      // scale < 0: use -q
   VarlenRef varlen;  // cu_q == nullptr: dense [B, H, N, d] layout (bf16 only otherwise)
+  float scale_abs = 0.f;  // |scale|: the fp32 kernel forms its coefficient in fp64 from it
 };
 
 // Paged KV cache: k/v point at page pools [num_pages, Hkv, page_size, d];

@@ -20,8 +20,10 @@
 // (about 1e-5 at N = 2800, |o| = 4), and the 128-term fp32 dot product puts
 // ~5e-6 (log2 units) into each exponent at |scale| = 0.45, which a sharp
 // softmax turns into ~1e-5 of output error; products of fp32 values are exact
-// in fp64.  What is left is the fp32 exponentials and the fp32 coefficient
-// c, about 1e-6 of the output and of lse.
+// in fp64.  The coefficient c = |scale| log2(e) is formed in fp64 too: in
+// fp32 its rounding (2^-24 relative) times a row max of a few hundred (log2
+// units) moves lse by ~1e-5.  What is left is the fp32 exponentials, about
+// 1e-6 of the output, and lse's own fp32 rounding.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,7 +37,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, int n_qtiles, int BH,
-    float c, float qsign) {
+    double cd, float qsign) {
   __shared__ float qs[kF32Rows][D + 1];
   __shared__ float ks[kF32Keys][D];
   __shared__ float vs[kF32Keys][D];
@@ -63,7 +65,6 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(
   }
 #pragma unroll
   for (int i = 0; i < D; ++i) acc[i] = 0.0;
-  const double cd = (double)c;
   double m_run = -INFINITY;  // running max of c * (q . k), log2 units
   double l_run = 0.0;
 
@@ -116,6 +117,13 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(
   if (lse != nullptr) lse[(size_t)bh * N + row] = (float)(m_run * 0.6931471805599453 + log(l_run));
 }
 
+// c = |scale| log2(e) in fp64, clamped below at kMinC as the bf16 kernels' c is
+// (so that c * (-inf) stays -inf at a zero scale)
+double f32_coeff(float scale_abs) {
+  const double c = (double)scale_abs * 1.4426950408889634074;
+  return c < (double)kMinC ? (double)kMinC : c;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kF32Rows - 1) / kF32Rows;
@@ -125,7 +133,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kF32Rows), 0, stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                      static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Hq, a.Hkv, a.N,
-                     n_qtiles, BH, a.c, a.neg ? -1.0f : 1.0f);
+                     n_qtiles, BH, f32_coeff(a.scale_abs), a.neg ? -1.0f : 1.0f);
   return hipGetLastError();
 }
 

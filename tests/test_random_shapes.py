@@ -26,6 +26,19 @@ from gpu_util import BF16_LSE_MAX_ABS, F32_LSE_MAX_ABS, F32_MAX_ABS, check_bf16_
 pytestmark = pytest.mark.gpu
 
 
+def fp32(x):
+    """A drawn scale as the fp32 value the kernels receive (the oracle widens that value)."""
+    return float(np.float32(x))
+
+
+def check_f32_lse(lse_gpu, lse_ref, what):
+    """fp32 lse: 1e-5 plus one ulp of the fp32 output, whose half-ulp alone is 7.6e-6 at
+    |lse| = 128 and 1.5e-5 at 256 (the sharp softmaxes of the larger drawn scales)."""
+    err = np.abs(f64(lse_gpu) - lse_ref)
+    bound = F32_LSE_MAX_ABS + 2.0 ** -23 * np.abs(lse_ref)
+    assert np.isfinite(err).all() and (err <= bound).all(), f"{what}: max excess {(err - bound).max():.3e}"
+
+
 def _dense_cases(n, seed):
     rng = random.Random(seed)
     cases = []
@@ -47,7 +60,7 @@ def _dense_cases(n, seed):
 def test_random_dense_prefill_bf16(B, Hkv, G, N, d, causal, scale, seed):
     print(f"dense bf16 B{B} Hkv{Hkv} G{G} N{N} d{d} causal={causal} scale={scale}", flush=True)
     q, k, v, s0 = I.prefill_inputs(B, Hkv * G, Hkv, N, d, "bf16", seed=seed)
-    scale = s0 if scale is None else scale
+    scale = s0 if scale is None else fp32(scale)
     o, lse = prefill(*to_dev(q, k, v), causal=causal, scale=scale)
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, causal, scale)
@@ -60,12 +73,12 @@ def test_random_dense_prefill_bf16(B, Hkv, G, N, d, causal, scale, seed):
 def test_random_dense_prefill_f32(B, Hkv, G, N, d, causal, scale, seed):
     print(f"dense f32 B{B} Hkv{Hkv} G{G} N{N} d{d} causal={causal} scale={scale}", flush=True)
     q, k, v, s0 = I.prefill_inputs(B, Hkv * G, Hkv, N, d, "f32", seed=seed)
-    scale = s0 if scale is None else scale
+    scale = s0 if scale is None else fp32(scale)
     o, lse = prefill(*to_dev(q, k, v), causal=causal, scale=scale)
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, causal, scale)
     check_close(o, ro, F32_MAX_ABS, "o")
-    check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
+    check_f32_lse(lse, rl, "lse")
 
 
 def _wide_cases(n, seed):
@@ -181,7 +194,7 @@ def test_random_backward(B, Hkv, G, N, d, causal, scale, seed):
     """dq, dk, dv against the oracle's backward, with the bar of tests/test_backward.py."""
     print(f"backward B{B} Hkv{Hkv} G{G} N{N} d{d} causal={causal} scale={scale}", flush=True)
     q, k, v, do, s0 = I.backward_inputs(B, Hkv * G, Hkv, N, d, seed=seed)
-    scale = s0 if scale is None else scale
+    scale = s0 if scale is None else fp32(scale)
     qd, kd, vd, dod = to_dev(q, k, v, do)
     o, lse = prefill(qd, kd, vd, causal=causal, scale=scale)
     grads = prefill_backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)

@@ -94,6 +94,7 @@ def test_bf16_causal_row0_is_exact():
 @pytest.mark.parametrize("scale", [-0.0883883, 0.0, 3.0])
 def test_bf16_scale_sign_zero_and_large(scale):
     """Negative scale, zero scale (uniform weights) and scores near 1e3 (no overflow)."""
+    scale = float(np.float32(scale))  # the fp32 value the kernel receives, which the oracle widens
     q, k, v, _ = I.prefill_inputs(1, 4, 2, 200, 128, "bf16", seed=13)
     for causal in (False, True):
         o, lse = gpu_prefill(q, k, v, causal, scale)
@@ -269,6 +270,7 @@ def test_decode_scale_sign_zero_and_large(dtype, G, scale):
     """Negative scale (query signs flipped, positive exponent coefficient),
     zero scale (uniform weights over the visible keys) and scores near 1e2
     (no overflow), for both decode paths."""
+    scale = float(np.float32(scale))  # the fp32 value the kernel receives, which the oracle widens
     lens = [1, 31, 33, 300, 1024, 1300, 5]
     q, kc, vc, ls, _ = I.decode_inputs(len(lens), 2 * G, 2, 128, 1, 1300, 1300, dtype, seed=70 + G, seqlens=lens)
     o = gpu_decode(q, kc, vc, ls, scale)

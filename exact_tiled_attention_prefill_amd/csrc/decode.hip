@@ -30,8 +30,11 @@
 //       four waves are merged once per chunk through LDS.
 //     Each (sequence, head) row's chunk order is rotated by the row index so
 //     that the XCDs receive equal shares of real chunks.
-//     fp32 path (512-key chunks): VGPR loads and fp32 FMAs, 4 lanes per row
-//       for scores and 16 (or 32) lanes per row for values.
+//     fp32 path (512-key chunks): VGPR loads, 4 lanes per row for scores and
+//       16 (or 32) lanes per row for values; the score dot products, chunk
+//       max, probability sum and P.V sums are taken in fp64 (fp32 inputs,
+//       fp32 probabilities from exp2f), so that rounding stays far below
+//       fp32 output tolerance even where large scores amplify it.
 //     Both paths load the cache with the non-temporal hint: every byte is read
 //     once, and marking its lines evict-first raised the bf16 split kernel
 //     from ~5.6 to ~6.0 TB/s on MI355X (a plain read stream reaches ~6.3 TB/s,
@@ -44,6 +47,7 @@
 // seqlens is read only on the device; chunks at or past a sequence's length
 // exit at once, rows past the length are never loaded.
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -96,6 +100,7 @@ struct Elem<float> {
 };
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+__device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, 64); }
 
 // grid: x = chunk index, y = kv head * (G/GT) + head slice, z = sequence.
 template <typename T, int D, int GT>
@@ -112,9 +117,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   static_assert(64 % kVLanes == 0, "row must split over lanes");
 
   __shared__ float p_lds[kChunk][GT];
-  __shared__ float red_m[kWaves][GT];
-  __shared__ float red_l[kWaves][GT];
-  __shared__ float o_lds[kWaves][GT][D];
+  __shared__ double red_m[kWaves][GT];
+  __shared__ double red_l[kWaves][GT];
+  __shared__ double o_lds[kWaves][GT][D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // passes whose loads are issued together (<= 128 VGPRs of loads in flight)
   constexpr int kSB = (32 / kSLoads) < kPasses ? (32 / kSLoads) : kPasses;
   static_assert(kPasses % kSB == 0, "score passes must batch evenly");
-  float sc[kPasses][GT];
+  double sc[kPasses][GT];
 #pragma unroll
   for (int p0 = 0; p0 < kPasses; p0 += kSB) {
     u32x4 buf[kSB][kSLoads];
@@ -170,9 +175,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kSB; ++i) {
-      float acc[GT];
+      double acc[GT];
 #pragma unroll
-      for (int g = 0; g < GT; ++g) acc[g] = 0.f;
+      for (int g = 0; g < GT; ++g) acc[g] = 0.0;
 #pragma unroll
       for (int cc = 0; cc < kSLoads; ++cc) {
         float kf[kE];
@@ -180,30 +185,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < kE; ++e)
 #pragma unroll
-          for (int g = 0; g < GT; ++g) acc[g] = fmaf(kf[e], qv[g][cc * kE + e], acc[g]);
+          for (int g = 0; g < GT; ++g) acc[g] = fma((double)kf[e], (double)qv[g][cc * kE + e], acc[g]);
       }
       const int row = wave * kRowsPerWave + (p0 + i) * 16 + rs;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        float a = acc[g];
-        a += shfl_xor_f(a, 1);
-        a += shfl_xor_f(a, 2);
-        sc[p0 + i][g] = row < n ? a * c : -INFINITY;
+        double a = acc[g];
+        a += shfl_xor_d(a, 1);
+        a += shfl_xor_d(a, 2);
+        sc[p0 + i][g] = row < n ? a * (double)c : -INFINITY;
       }
     }
   }
 
   // chunk max per head
-  float mloc[GT];
+  double mloc[GT];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    float mx = -INFINITY;
+    double mx = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) mx = fmaxf(mx, sc[p][g]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 4));
-    mx = fmaxf(mx, shfl_xor_f(mx, 8));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    for (int p = 0; p < kPasses; ++p) mx = fmax(mx, sc[p][g]);
+    mx = fmax(mx, shfl_xor_d(mx, 4));
+    mx = fmax(mx, shfl_xor_d(mx, 8));
+    mx = fmax(mx, shfl_xor_d(mx, 16));
+    mx = fmax(mx, shfl_xor_d(mx, 32));
     mloc[g] = mx;
   }
   if (lane == 0) {
@@ -211,24 +216,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int g = 0; g < GT; ++g) red_m[wave][g] = mloc[g];
   }
   __syncthreads();
-  float M[GT];
+  double M[GT];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    float mx = red_m[0][g];
+    double mx = red_m[0][g];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red_m[w][g]);
+    for (int w = 1; w < kWaves; ++w) mx = fmax(mx, red_m[w][g]);
     M[g] = mx;  // finite: the chunk has at least one row
   }
   // probabilities to LDS, partial sums
-  float lpart[GT];
+  double lpart[GT];
 #pragma unroll
-  for (int g = 0; g < GT; ++g) lpart[g] = 0.f;
+  for (int g = 0; g < GT; ++g) lpart[g] = 0.0;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int row = wave * kRowsPerWave + p * 16 + rs;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const float e = fast_exp2(sc[p][g] - M[g]);
+      const float e = exp2f((float)(sc[p][g] - M[g]));
       if (jq == 0) {
         p_lds[row][g] = e;
         lpart[g] += e;
@@ -237,11 +242,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    float s = lpart[g];
-    s += shfl_xor_f(s, 4);
-    s += shfl_xor_f(s, 8);
-    s += shfl_xor_f(s, 16);
-    s += shfl_xor_f(s, 32);
+    double s = lpart[g];
+    s += shfl_xor_d(s, 4);
+    s += shfl_xor_d(s, 8);
+    s += shfl_xor_d(s, 16);
+    s += shfl_xor_d(s, 32);
     if (lane == 0) red_l[wave][g] = s;
   }
   __syncthreads();
@@ -249,11 +254,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // ---------------- values: kVLanes lanes per row ----------------
   const int vs = lane / kVLanes;  // row slot
   const int vd = lane % kVLanes;  // 16-byte column
-  float oacc[GT][kE];
+  double oacc[GT][kE];
 #pragma unroll
   for (int g = 0; g < GT; ++g)
 #pragma unroll
-    for (int e = 0; e < kE; ++e) oacc[g][e] = 0.f;
+    for (int e = 0; e < kE; ++e) oacc[g][e] = 0.0;
   constexpr int kVPasses = kRowsPerWave / kVSlots;
   constexpr int kBatch = 16;
   static_assert(kVPasses % kBatch == 0, "value passes must batch evenly");
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         for (int g = 0; g < GT; ++g) {
           const float pg = p_lds[row][g];
 #pragma unroll
-          for (int e = 0; e < kE; ++e) oacc[g][e] = fmaf(pg, vf[e], oacc[g][e]);
+          for (int e = 0; e < kE; ++e) oacc[g][e] = fma((double)pg, (double)vf[e], oacc[g][e]);
         }
       }
     }
@@ -288,9 +293,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   for (int g = 0; g < GT; ++g)
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-      float a = oacc[g][e];
+      double a = oacc[g][e];
 #pragma unroll
-      for (int m = kVLanes; m < 64; m <<= 1) a += shfl_xor_f(a, m);
+      for (int m = kVLanes; m < 64; m <<= 1) a += shfl_xor_d(a, m);
       oacc[g][e] = a;
     }
   if (vs == 0) {
@@ -303,15 +308,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // final: thread t handles (g, d) pairs
   for (int i = tid; i < GT * D; i += 256) {
     const int g = i / D, d = i % D;
-    float l = 0.f, a = 0.f;
+    double l = 0.0, a = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       l += red_l[w][g];
       a += o_lds[w][g][d];
     }
     const size_t pidx = ((size_t)b * Hq + h0 + g) * nsplit + split;
-    part_o[pidx * D + d] = a / l;
-    if (d == 0) part_lse[pidx] = M[g] * kLn2 + __logf(l);
+    part_o[pidx * D + d] = (float)(a / l);
+    if (d == 0) part_lse[pidx] = (float)(M[g] * 0.6931471805599453 + log(l));
   }
 }
 
@@ -364,7 +369,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const int nb = min(kCombBatch, ns - s0);
     __syncthreads();  // previous batch's weights fully read (and red[] read above)
     for (int i = tid; i < nb; i += kCombThreads) {
-      const float w = __expf(lse[s0 + i] - mx);
+      // the fp32 path takes the accurate exponential (about 1 ulp), bf16 the fast
+      // one, whose error grows with |argument|
+      const float w = std::is_same<T, float>::value ? expf(lse[s0 + i] - mx) : __expf(lse[s0 + i] - mx);
       w_lds[i] = w;
       wpart += w;
     }
@@ -739,10 +746,15 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Heads per block: 4 at d = 64; at d = 128 the fp32 query slices of 4 heads
+// (128 VGPRs) beside their fp64 scores and the loads in flight would spill,
+// so 2.
 template <typename T, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_t<T, D, 4>(a, stream);
+  if constexpr (D <= 64) {
+    if (G % 4 == 0) return launch_t<T, D, 4>(a, stream);
+  }
   if (G % 2 == 0) return launch_t<T, D, 2>(a, stream);
   return launch_t<T, D, 1>(a, stream);
 }

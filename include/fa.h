@@ -185,7 +185,10 @@ int fa_decode_ws(const void* q, const void* kcache, const void* vcache,
                  int maxlen, int d, float scale, void* workspace,
                  size_t workspace_bytes, void* stream);
 
-/* Decode with fp32 q/caches/o (same layouts and semantics). */
+/* Decode with fp32 q/caches/o (same layouts and semantics).  Scores, chunk
+ * maxima, sums and P.V accumulate in fp64 over fp32 inputs; probabilities,
+ * stored partials and the output are fp32: within about 1e-5 of the exact
+ * result for unit-scale caches. */
 int fa_decode_f32(const float* q, const float* kcache, const float* vcache,
                   const int32_t* seqlens, float* o, int B, int Hq, int Hkv,
                   int maxlen, int d, float scale, void* stream);

@@ -281,6 +281,29 @@ def test_decode_scale_sign_zero_and_large(dtype, G, scale):
         check_bf16(o, ro, "decode bf16 scale")
 
 
+@pytest.mark.parametrize("kind", ["large", "falling"])
+@pytest.mark.parametrize("lens,d,G,scale", [([35, 20, 1], 128, 4, 0.1416), ([6517, 3000], 128, 4, 0.0884),
+                                           ([30000, 513], 64, 8, 0.125)])
+def test_decode_f32_sharp_scores(kind, lens, d, G, scale):
+    """fp32 decode where rounding is amplified: q and K scaled by 4 (scores
+    spread over tens of units, one or two keys carrying the weight), or scores
+    falling along the cache (the first entry holds the max and the later
+    chunks' weights fall to e^-60 and below).  A single split (35 keys) and
+    several, both head dims, held to the fp32 bar."""
+    scale = float(np.float32(scale))
+    q, kc, vc, ls, _ = I.decode_inputs(len(lens), 2 * G, 2, d, 1, max(lens), max(lens), "f32", seed=90 + d,
+                                       seqlens=lens)
+    if kind == "large":
+        q, kc = q * 4, kc * 4
+    else:
+        sgn = torch.sign(torch.randn((d,), generator=torch.Generator().manual_seed(d)))
+        ramp = torch.linspace(6, 0, max(lens))[None, None, :, None]
+        q, kc = q * 0.2 + sgn, kc * 0.2 + ramp * sgn
+    o = gpu_decode(q, kc, vc, ls, scale)
+    ro, _ = oracle.decode(q, kc, vc, ls, scale)
+    check_close(o, ro, F32_MAX_ABS, f"decode f32 {kind}")
+
+
 def test_decode_matches_last_prefill_row():
     """Decode of token i against K,V[0..i] equals causal prefill row i (both on the GPU)."""
     q, k, v, scale = I.prefill_inputs(2, 8, 2, 700, 128, "bf16", seed=23)

@@ -41,6 +41,12 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Performance goals, as fractions of those peaks: compute-bound prefill at
+# least half the dense bf16 matrix rate, bandwidth-bound decode at least 70%
+# of HBM bandwidth.  Each leg reports its goal and whether it was met; the
+# backward has no stated goal.
+GOAL_PREFILL_FRAC = 0.5
+GOAL_DECODE_FRAC = 0.7
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_prefill_amd", "csrc")
 PREFILL_SRC = os.path.join(CSRC, "prefill_bf16.hip")
@@ -442,9 +448,16 @@ def stats(ms):
     return {"ms_avg": sum(ms) / k, "ms_median": ms[k // 2], "ms_min": ms[0], "launches": k}
 
 
-def mfma_roofline(kernel, tflops, counters_name=None, src=PREFILL_SRC, algorithmic_bytes=None):
-    rl = {"kernel": kernel, "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-          "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}
+def with_goal(rl, goal):
+    rl["goal_frac"] = goal
+    rl["goal_met"] = None if goal is None else bool(rl["frac"] >= goal)
+    return rl
+
+
+def mfma_roofline(kernel, tflops, counters_name=None, src=PREFILL_SRC, algorithmic_bytes=None,
+                  goal=GOAL_PREFILL_FRAC):
+    rl = with_goal({"kernel": kernel, "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None}, goal)
     if algorithmic_bytes is not None:
         rl["algorithmic_bytes"] = algorithmic_bytes
     if counters_name is not None:
@@ -582,10 +595,12 @@ def main():
         result["decode_paged"] = dict(workload=dc.name + f"-paged{args.page_size}", page_size=args.page_size, **st,
                                       GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS, bytes_per_launch=nbytes,
                                       tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
-                                      roofline={"kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
-                                                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                                "frac": gbs / PEAK_HBM_GBS,
-                                                "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)})
+                                      roofline=with_goal({
+                                          "kernel": "decode_bf16_mfma_kernel<paged> + decode_combine_kernel",
+                                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                          "frac": gbs / PEAK_HBM_GBS,
+                                          "traffic": measured_traffic("decode_paged_counters", DECODE_SRC)},
+                                          GOAL_DECODE_FRAC))
         if pool is not None:
             host["decode_paged_out"] = pgo.cpu()
         del kpd, vpd, pws
@@ -647,7 +662,7 @@ def main():
                                           "kernels": "dQ (with the D and lse rows) + dK/dV"}, **st, tflops=tf,
                                   flops_per_launch=flops,
                                   roofline=mfma_roofline("bwd_dq_kernel + bwd_dkdv_kernel", tf, "backward_counters",
-                                                         src=BACKWARD_SRC))
+                                                         src=BACKWARD_SRC, goal=None))
         if result["value"] is None:
             result["value"] = tf
         if pool is not None:
@@ -705,13 +720,14 @@ def main():
             result["decode"] = dict(workload=dc.name, **st, GB_per_s=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS,
                                     bytes_per_launch=nbytes, tokens_per_s=dc.B / (st["ms_avg"] * 1e-3),
                                     device_memory=d_mem,
-                                    roofline={"kernel": "decode_bf16_mfma_kernel + decode_combine_kernel",
-                                              "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                              "frac": gbs / PEAK_HBM_GBS,
-                                              "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
-                                              "rocprof": measured_counters("decode_gqa_counters", DECODE_SRC,
-                                                                           ("hbm_gbs_counter_run",
-                                                                            "shader_clock_ghz"))})
+                                    roofline=with_goal({
+                                        "kernel": "decode_bf16_mfma_kernel + decode_combine_kernel",
+                                        "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": gbs / PEAK_HBM_GBS,
+                                        "traffic": measured_traffic("decode_gqa_counters", DECODE_SRC),
+                                        "rocprof": measured_counters("decode_gqa_counters", DECODE_SRC,
+                                                                     ("hbm_gbs_counter_run", "shader_clock_ghz"))},
+                                        GOAL_DECODE_FRAC))
             if result["value"] is None:
                 result["value"], result["unit"] = gbs, "GB/s"
             if pool is not None:

@@ -147,3 +147,13 @@ def test_backward_parity_check(pool):
     bad[2][0, 1, 33, 5] += 0.5
     err, _ = bench.oracle_backward_check(pool, q, k, v, do, s, bad)
     assert not err["within_bar"] and err["dv"]["max_abs_over_range"] > 2e-2
+
+
+def test_rooflines_state_their_goal():
+    rl = bench.mfma_roofline("k", 0.49 * bench.PEAK_BF16_TFLOPS)
+    assert rl["goal_frac"] == 0.5 and rl["goal_met"] is False
+    assert bench.mfma_roofline("k", 0.5 * bench.PEAK_BF16_TFLOPS)["goal_met"] is True
+    none = bench.mfma_roofline("k", 1.0, goal=None)
+    assert none["goal_frac"] is None and none["goal_met"] is None
+    hbm = bench.with_goal({"frac": 0.83}, bench.GOAL_DECODE_FRAC)
+    assert hbm["goal_frac"] == 0.7 and hbm["goal_met"] is True

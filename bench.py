@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP64_VALU_TFLOPS = 78.6  # MI355X fp64 vector: 256 CU x 4 SIMD x 16 lanes x 2 FLOP (FMA) x 2.4 GHz
 # Performance goals, as fractions of those peaks: compute-bound prefill at
 # least half the dense bf16 matrix rate, bandwidth-bound decode at least 70%
 # of HBM bandwidth.  Each leg reports its goal and whether it was met; the
@@ -54,6 +55,7 @@ DECODE_SRC = os.path.join(CSRC, "decode.hip")
 BACKWARD_SRC = os.path.join(CSRC, "backward_bf16.hip")
 BAR = {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3}
 # backward: the forward's bf16 bar scaled to each gradient's range s = max(1, max|ref|)
+F32_BAR = {"o_max_abs": 1e-5, "lse_max_abs": 1e-5}
 BWD_BAR = {"max_abs_over_range": 2e-2, "mean_abs_over_range": 2e-3}
 PREFILL_KERNEL = "prefill_bf16_kernel<128, causal> (4 or 8 waves per workgroup, as the launcher picks)"
 
@@ -217,6 +219,28 @@ def _oracle_job(job):
         emax, esum, count, lmax = max(emax, float(e.max())), esum + float(e.sum()), count + e.size, max(
             lmax, float(el.max()))
     return flops, emax, esum, count, lmax
+
+
+def _oracle_f32_job(job):
+    """A whole fp32 prefill through the fp64 oracle (run in a pool worker) and
+    the GPU output's largest errors.  Tensors arrive as float32 arrays."""
+    import numpy as np
+
+    import oracle
+
+    q, k, v, causal, scale, o, lse = job
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    return float(np.abs(o.astype(np.float64) - ro).max()), float(np.abs(lse.astype(np.float64) - rl).max())
+
+
+def oracle_f32_check(pool, q, k, v, causal, scale, o_gpu, lse_gpu):
+    """Compare every element of an fp32 prefill with the oracle (one job)."""
+    t0 = time.perf_counter()
+    eo, el = pool.apply(_oracle_f32_job, ((q.numpy(), k.numpy(), v.numpy(), causal, scale, o_gpu.numpy(),
+                                           lse_gpu.numpy()),))
+    err = {"o_max_abs": eo, "lse_max_abs": el}
+    err["within_bar"] = all(err[key] <= F32_BAR[key] for key in F32_BAR)
+    return err, time.perf_counter() - t0
 
 
 def _oracle_bwd_job(job):
@@ -478,7 +502,8 @@ def main():
     ap.add_argument("--no-legs", action="store_true", help="time only the step (128K prefill + decode)")
     ap.add_argument("--page-size", type=int, default=64, help="page size of the paged-decode leg")
     ap.add_argument("--only", choices=["step", "prefill_gqa_128k", "decode", "prefill_mha_4k", "prefill_gqa_16k",
-                                       "decode_paged", "prefill_chunked", "prefill_window", "backward", "copy",
+                                       "decode_paged", "prefill_chunked", "prefill_window", "prefill_f32_small", "backward",
+                                       "copy",
                                        "ceiling"],
                     default=None,
                     help="run one kernel only (for profiler runs); 'step' runs the 128K prefill and the decode; "
@@ -641,6 +666,32 @@ def main():
         if result["value"] is None:
             result["value"] = tf
 
+    if leg("prefill_f32_small"):
+        # the small fp32 workload: one head, 256 rows, d = 64, no mask
+        fc = I.PREFILL_F32_SMALL
+        fq, fk, fv, fscale = I.prefill_config_inputs(fc)
+        fqd, fkd, fvd = fq.to(dev), fk.to(dev), fv.to(dev)
+        fod = torch.empty_like(fqd)
+        fld = torch.empty((fc.B, fc.Hq, fc.N), dtype=torch.float32, device=dev)
+
+        def ff():
+            prefill(fqd, fkd, fvd, causal=fc.causal, scale=fscale, out=fod, lse=fld)
+        warm(ff, args.warmup)
+        st = stats(time_calls(ff, stream, legs_steps))
+        F = prefill_flops(fc.B, fc.Hq, fc.N, fc.d, fc.causal)
+        tf = F / (st["ms_avg"] * 1e-3) / 1e12
+        result["prefill_f32_small"] = dict(
+            workload=fc.name, **st, tflops=tf, flops_per_launch=F, dtype="f32 in/out, f64 sums",
+            roofline=with_goal({"kernel": "prefill_f32_kernel", "bound": "alu", "achieved": tf,
+                                "peak": PEAK_FP64_VALU_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_FP64_VALU_TFLOPS,
+                                "traffic": None,
+                                "note": "fp64 FMAs for the dot products and sums; at this size the launch "
+                                        "fills only a few of the 256 CUs"}, None))
+        if pool is not None:
+            host["prefill_f32_small"] = (fq, fk, fv, fc.causal, fscale)
+            host["prefill_f32_small_out"] = (fod.cpu(), fld.cpu())
+        del fqd, fkd, fvd, fod, fld
+
     if leg("backward"):
         # backward of the MHA 4K causal workload: the forward's o and lse feed it
         bc = I.PREFILL_MHA_4K
@@ -790,6 +841,9 @@ def main():
                                                   f"the 2 longest, seeded others) x {dc.Hq} heads",
                                                   bar={"o_max_abs": BAR["o_max_abs"], "o_mean_abs": BAR["o_mean_abs"]},
                                                   oracle_seconds=dt, **err)
+        if "prefill_f32_small_out" in host:
+            err, dt = oracle_f32_check(pool, *host["prefill_f32_small"], *host["prefill_f32_small_out"])
+            parity[I.PREFILL_F32_SMALL.name] = dict(rows="every element", bar=F32_BAR, oracle_seconds=dt, **err)
         if "backward_out" in host:
             bq, bk, bv, bdo, bscale = host["backward"]
             err, dt = oracle_backward_check(pool, bq, bk, bv, bdo, bscale, host["backward_out"])

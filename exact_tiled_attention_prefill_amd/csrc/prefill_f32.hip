@@ -8,10 +8,15 @@
 // During Local Inference?", "Kernel Fusion Keeps More of the Attention Chain
 // in One Execution Path").
 //
-// Layout: one thread per query row, 128 rows per workgroup; the output
-// accumulator in registers, the rows' q in LDS (padded by one word, so the
-// 128 threads' reads of their own rows fall in different banks), 32-key fp32
-// K/V tiles in LDS read as broadcasts.
+// Layout: a workgroup takes 16 query rows of one head; each of its 4 or 8
+// waves covers all 16 rows (4 lanes per row, each lane a quarter of d in
+// interleaved 16-byte pieces) and takes every 4th (8th) 8-key batch of the keys,
+// keeping its own running max, sum and output for the rows.  q and the output
+// accumulator stay in registers (fp64); K and V rows come straight from
+// memory, the 16 rows of a wave reading the same 16-byte pieces.  The
+// waves' states are merged through LDS at the end with weights 2^(m_w - M)
+// (the running-softmax rule applied to whole key subsets).  Small problems
+// thus still spread over many waves: one head of 256 rows is 128 waves.
 //
 // Precision: fp32 inputs and outputs, fp64 sums.  The scores q.k, the
 // running max, the output accumulator and the running sum are fp64, and the
@@ -30,91 +35,143 @@
 namespace fa {
 namespace {
 
-constexpr int kF32Rows = 128;
-constexpr int kF32Keys = 32;
+constexpr int kF32Rows = 16;   // query rows per workgroup
+constexpr int kF32Batch = 8;   // keys per batch (one max and one rescale per batch)
+// Waves per workgroup (SPLIT), each taking every SPLIT-th key batch: 8 while
+// the grid is small (one head of 256 rows: 57 -> 36 us on MI355X), 4 for
+// large grids, where at d = 128 the 8-wave form fits only one workgroup per
+// CU (3-7% slower there).
+constexpr int kF32SmallGrid = 4096;  // workgroups below which 8 waves are used
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(128) void prefill_f32_kernel(
+__device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, 64); }
+
+template <int D, bool CAUSAL, int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, int n_qtiles, int BH,
     double cd, float qsign) {
-  __shared__ float qs[kF32Rows][D + 1];
-  __shared__ float ks[kF32Keys][D];
-  __shared__ float vs[kF32Keys][D];
+  constexpr int kC = D / 16;  // 16-byte pieces of a row per lane
+  constexpr int kL = D / 4;   // elements of a row per lane
+  __shared__ double red_m[SPLIT][kF32Rows];
+  __shared__ double red_l[SPLIT][kF32Rows];
+  __shared__ double red_o[SPLIT][kF32Rows][D];
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int rl = lane >> 2;   // row of the workgroup
+  const int part = lane & 3;  // quarter of d: elements 16c + 4part + e
   const int bid = blockIdx.x;
-  const int qtile = CAUSAL ? (n_qtiles - 1 - bid / BH) : (bid / BH);
+  const int qtile = CAUSAL ? (n_qtiles - 1 - bid / BH) : (bid / BH);  // causal: long rows first
   const int bh = bid % BH;
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
-  const float* qh = q + (size_t)bh * N * D;
   const float* kh = k + ((size_t)b * Hkv + g) * N * D;
   const float* vh = v + ((size_t)b * Hkv + g) * N * D;
 
   const int q0 = qtile * kF32Rows;
-  const int row = q0 + tid;
-  const bool live = row < N;
-
-  double acc[D];
-  // q rows of the workgroup into LDS (coalesced: consecutive threads read
-  // consecutive elements)
-  for (int e = tid; e < kF32Rows * D; e += kF32Rows) {
-    const int r = e / D, cc = e % D;
-    qs[r][cc] = q0 + r < N ? qsign * qh[(size_t)(q0 + r) * D + cc] : 0.f;
-  }
+  const int row = q0 + rl;  // rows past N compute on row N-1 and are not stored
+  double qd[kL];
+  {
+    const float* qr = q + ((size_t)bh * N + min(row, N - 1)) * D + 4 * part;
 #pragma unroll
-  for (int i = 0; i < D; ++i) acc[i] = 0.0;
+    for (int c = 0; c < kC; ++c) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qr + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qd[4 * c + e] = (double)(qsign * x[e]);
+    }
+  }
+  double acc[kL];
+#pragma unroll
+  for (int i = 0; i < kL; ++i) acc[i] = 0.0;
   double m_run = -INFINITY;  // running max of c * (q . k), log2 units
   double l_run = 0.0;
 
   const int kv_end = CAUSAL ? min(N, q0 + kF32Rows) : N;
-  for (int k0 = 0; k0 < kv_end; k0 += kF32Keys) {
-    __syncthreads();
-    for (int i = tid; i < kF32Keys * D; i += kF32Rows) {
-      const int r = i / D, cc = i % D;
-      const bool ok = k0 + r < N;
-      ks[r][cc] = ok ? kh[(size_t)(k0 + r) * D + cc] : 0.f;
-      vs[r][cc] = ok ? vh[(size_t)(k0 + r) * D + cc] : 0.f;
-    }
-    __syncthreads();
-    // s[j] = q . k_j in fp64, summed over i in order
-    double s[kF32Keys];
+  const int nb = (kv_end + kF32Batch - 1) / kF32Batch;
+  for (int bt = wave; bt < nb; bt += SPLIT) {
+    const int k0 = bt * kF32Batch;
+    // s[j] = q . k_j in fp64: a quarter of the terms per lane, then the
+    // quarters summed across the row's 4 lanes (the same value in each)
+    double s[kF32Batch];
 #pragma unroll
-    for (int j = 0; j < kF32Keys; ++j) s[j] = 0.0;
-    for (int i = 0; i < D; ++i) {
-      const double qi = (double)qs[tid][i];
+    for (int j = 0; j < kF32Batch; ++j) {
+      const int key = k0 + j;
+      const float* kr = kh + (size_t)min(key, N - 1) * D + 4 * part;
+      double a = 0.0;
 #pragma unroll
-      for (int j = 0; j < kF32Keys; ++j) s[j] = fma(qi, (double)ks[j][i], s[j]);
+      for (int c = 0; c < kC; ++c) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(kr + 16 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a = fma(qd[4 * c + e], (double)x[e], a);
+      }
+      a += shfl_xor_d(a, 1);
+      a += shfl_xor_d(a, 2);
+      const bool masked = key >= N || (CAUSAL && key > row);
+      s[j] = masked ? -INFINITY : a;
     }
     double mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kF32Keys; ++j) {
-      const int key = k0 + j;
-      const bool masked = key >= N || (CAUSAL && key > row);
-      s[j] = masked ? -INFINITY : s[j];
-      mx = fmax(mx, s[j]);
-    }
+    for (int j = 0; j < kF32Batch; ++j) mx = fmax(mx, s[j]);
     const double mn = fmax(m_run, mx * cd);
-    if (mn == -INFINITY) continue;  // nothing visible yet (padding rows only)
-    const double alpha = (double)exp2f((float)(m_run - mn));
+    // a row that has seen no key yet keeps m = -inf, l = 0, o = 0
+    const double mref = mn == -INFINITY ? 0.0 : mn;
+    const double alpha = (double)exp2f((float)(m_run - mref));
     l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < D; ++i) acc[i] *= alpha;
+    for (int i = 0; i < kL; ++i) acc[i] *= alpha;
     m_run = mn;
 #pragma unroll
-    for (int j = 0; j < kF32Keys; ++j) {
-      const double p = (double)exp2f((float)fma(s[j], cd, -mn));
+    for (int j = 0; j < kF32Batch; ++j) {
+      const double p = (double)exp2f((float)fma(s[j], cd, -mref));
       l_run += p;
+      const float* vr = vh + (size_t)min(k0 + j, N - 1) * D + 4 * part;
 #pragma unroll
-      for (int i = 0; i < D; ++i) acc[i] = fma(p, (double)vs[j][i], acc[i]);
+      for (int c = 0; c < kC; ++c) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(vr + 16 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * c + e] = fma(p, (double)x[e], acc[4 * c + e]);
+      }
     }
   }
-  if (!live) return;
-  const double inv = 1.0 / l_run;
+
+  // merge the waves' states of each row
+  if (part == 0) {
+    red_m[wave][rl] = m_run;
+    red_l[wave][rl] = l_run;
+  }
 #pragma unroll
-  for (int i = 0; i < D; ++i) o[(size_t)bh * N * D + (size_t)row * D + i] = (float)(acc[i] * inv);
-  if (lse != nullptr) lse[(size_t)bh * N + row] = (float)(m_run * 0.6931471805599453 + log(l_run));
+  for (int c = 0; c < kC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red_o[wave][rl][16 * c + 4 * part + e] = acc[4 * c + e];
+  __syncthreads();
+  constexpr int kTPR = 64 * SPLIT / kF32Rows;  // merge threads per row
+  static_assert(D % kTPR == 0, "a row's columns split evenly over its threads");
+  const int rr = tid / kTPR;  // columns cc, cc + kTPR, ...
+  const int cc = tid % kTPR;
+  const int orow = q0 + rr;
+  if (orow >= N) return;
+  double M = red_m[0][rr];
+#pragma unroll
+  for (int w = 1; w < SPLIT; ++w) M = fmax(M, red_m[w][rr]);  // finite: wave 0 saw key 0
+  double wgt[SPLIT];
+  double l = 0.0;
+#pragma unroll
+  for (int w = 0; w < SPLIT; ++w) {
+    wgt[w] = exp2(red_m[w][rr] - M);  // 0 for a wave that saw none of the row's keys
+    l += wgt[w] * red_l[w][rr];
+  }
+  const double inv = 1.0 / l;
+  float* orow_p = o + ((size_t)bh * N + orow) * D;
+#pragma unroll
+  for (int i = 0; i < D / kTPR; ++i) {
+    const int col = cc + kTPR * i;
+    double a = 0.0;
+#pragma unroll
+    for (int w = 0; w < SPLIT; ++w) a = fma(wgt[w], red_o[w][rr][col], a);
+    orow_p[col] = (float)(a * inv);
+  }
+  if (lse != nullptr && cc == 0) lse[(size_t)bh * N + orow] = (float)(M * 0.6931471805599453 + log(l));
 }
 
 // c = |scale| log2(e) in fp64, clamped below at kMinC as the bf16 kernels' c is
@@ -124,17 +181,23 @@ double f32_coeff(float scale_abs) {
   return c < (double)kMinC ? (double)kMinC : c;
 }
 
+template <int D, bool CAUSAL, int SPLIT>
+hipError_t launch_split(const PrefillArgs& a, hipStream_t stream, int n_qtiles, int BH, unsigned blocks) {
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL, SPLIT>), dim3(blocks), dim3(64 * SPLIT), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Hq, a.Hkv, a.N,
+                     n_qtiles, BH, f32_coeff(a.scale_abs), a.neg ? -1.0f : 1.0f);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kF32Rows - 1) / kF32Rows;
   const int BH = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * BH;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kF32Rows), 0, stream,
-                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                     static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Hq, a.Hkv, a.N,
-                     n_qtiles, BH, f32_coeff(a.scale_abs), a.neg ? -1.0f : 1.0f);
-  return hipGetLastError();
+  return blocks < kF32SmallGrid ? launch_split<D, CAUSAL, 8>(a, stream, n_qtiles, BH, (unsigned)blocks)
+                                : launch_split<D, CAUSAL, 4>(a, stream, n_qtiles, BH, (unsigned)blocks);
 }
 
 }  // namespace

@@ -85,7 +85,9 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* Prefill with fp32 q/k/v/o (same layouts and semantics).  Scores, running max
  * and sums are formed in fp64 and the exponentials in fp32, so the result stays
- * within about 1e-6 of the exact one also for long rows and sharp softmaxes. */
+ * within about 1e-6 of the exact one also for long rows and sharp softmaxes.
+ * Work: one kernel launch on `stream` (16 query rows per workgroup, the keys
+ * split over its waves and merged at the end). */
 int fa_prefill_f32(const float* q, const float* k, const float* v, float* o,
                    float* lse, int B, int Hq, int Hkv, int N, int d, int causal,
                    float scale, void* stream);

@@ -157,3 +157,17 @@ def test_rooflines_state_their_goal():
     assert none["goal_frac"] is None and none["goal_met"] is None
     hbm = bench.with_goal({"frac": 0.83}, bench.GOAL_DECODE_FRAC)
     assert hbm["goal_frac"] == 0.7 and hbm["goal_met"] is True
+
+
+def test_f32_parity_check(pool):
+    q, k, v, s = I.prefill_inputs(1, 1, 1, 256, 64, "f32", seed=0)
+    ro, rl = oracle.attention(q, k, v, False, s)
+    o, lse = torch.from_numpy(ro.astype(np.float32)), torch.from_numpy(rl.astype(np.float32))
+    err, _ = bench.oracle_f32_check(pool, q, k, v, False, s, o, lse)
+    assert err["within_bar"] and err["o_max_abs"] < 1e-6
+    bad = o.clone()
+    bad[0, 0, 200, 3] += 3e-5
+    assert not bench.oracle_f32_check(pool, q, k, v, False, s, bad, lse)[0]["within_bar"]
+    bad_lse = lse.clone()
+    bad_lse[0, 0, 7] -= 3e-5
+    assert not bench.oracle_f32_check(pool, q, k, v, False, s, o, bad_lse)[0]["within_bar"]

@@ -62,6 +62,18 @@ def test_fp32_prefill_shapes(N, d, causal):
     check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
 
 
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_fp32_prefill_large_grid(d, causal):
+    """64 heads x 64 sixteen-row tiles = 4096 workgroups: the launch that takes
+    four waves per workgroup (the smaller grids above take eight), with a
+    ragged last tile."""
+    q, k, v, scale = I.prefill_inputs(1, 64, 8, 1020, d, "f32", seed=d)
+    o, lse = gpu_prefill(q, k, v, causal, scale)
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    check_close(o, ro, F32_MAX_ABS, "o")
+    check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
+
+
 # ------------------------------------------------------------------ bf16 prefill, small
 SMALL = [  # (B, Hkv, G, N, d)
     (1, 1, 1, 1, 128), (1, 1, 1, 2, 64), (2, 1, 2, 63, 128), (1, 2, 1, 64, 64), (1, 1, 4, 65, 128),

@@ -61,7 +61,8 @@ int prefill_common(const void* q, const void* k, const void* v, void* o, float* 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
   // grid limits: B*Hq*ceil(N/rows) workgroups must fit in 31 bits
-  if ((long long)B * Hq * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const int rows = bf16 ? fa::kPrefillBf16Rows : fa::kPrefillF32Rows;
+  if ((long long)B * Hq * ((N + rows - 1) / rows) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   st = check_device();
   if (st != FA_OK) return st;
   fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, softmax_coeff(scale), scale < 0.f};

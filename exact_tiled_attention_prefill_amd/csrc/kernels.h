@@ -98,6 +98,11 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 // Keys per split-KV chunk of the fp32 decode path (the bf16 path picks its
 // chunk per launch).
 constexpr int kDecodeChunk = 512;
+
+// Query rows per workgroup: the bf16 prefill kernels' tile (4 waves; 8-wave
+// launches take 256, so 128 bounds the grid) and the fp32 prefill kernel's.
+constexpr int kPrefillBf16Rows = 128;
+constexpr int kPrefillF32Rows = 16;
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d);
 
 // Allocation-free bf16 decode: the partials live in a fixed device array of

@@ -35,7 +35,7 @@
 namespace fa {
 namespace {
 
-constexpr int kF32Rows = 16;   // query rows per workgroup
+constexpr int kF32Rows = kPrefillF32Rows;  // query rows per workgroup
 constexpr int kF32Batch = 8;   // keys per batch (one max and one rescale per batch)
 // Waves per workgroup (SPLIT), each taking every SPLIT-th key batch: 8 while
 // the grid is small (one head of 256 rows: 57 -> 36 us on MI355X), 4 for

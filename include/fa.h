@@ -59,7 +59,9 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, Hq % Hkv != 0, scale not
                              finite or |scale|*log2(e) not finite in fp32,
-                             misaligned pointer, too-small workspace */
+                             misaligned pointer, too-small workspace, a grid
+                             of 2^31 or more workgroups (prefill: B*Hq*
+                             ceil(N/128) for bf16, ceil(N/16) for fp32) */
   FA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, or device is not gfx950 */
   FA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
   FA_ERR_NO_MEMORY = 4,   /* stream-ordered workspace allocation failed */

@@ -93,6 +93,16 @@ def test_prefill_rejects_invalid_arguments(name, kw, code):
     assert prefill_call(fn, **kw) == code
 
 
+@needs_lib
+def test_prefill_grid_limit_follows_each_kernels_tile():
+    # every call here fails validation (no device call): 2^20 heads x
+    # ceil(2^15 / 16) = 2^31 workgroups of the fp32 kernel's 16-row tiles;
+    # 2^24 heads x ceil(2^14 / 128) = 2^31 of the bf16 kernels' 128-row tiles
+    lib = binding.load_library()
+    assert prefill_call(lib.fa_prefill_f32, Hq=1 << 20, Hkv=1, N=1 << 15) == binding.FA_ERR_INVALID_ARG
+    assert prefill_call(lib.fa_prefill, Hq=1 << 24, Hkv=1, N=1 << 14) == binding.FA_ERR_INVALID_ARG
+
+
 def decode_call(fn, ws=False, **kw):
     a = dict(q=P, k=P, v=P, sl=P, o=P, B=2, Hq=8, Hkv=2, maxlen=1024, d=128, scale=0.1,
              w=P, wb=1 << 30)

@@ -30,11 +30,14 @@
 //       four waves are merged once per chunk through LDS.
 //     Each (sequence, head) row's chunk order is rotated by the row index so
 //     that the XCDs receive equal shares of real chunks.
-//     fp32 path (512-key chunks): VGPR loads, 4 lanes per row for scores and
-//       16 (or 32) lanes per row for values; the score dot products, chunk
-//       max, probability sum and P.V sums are taken in fp64 (fp32 inputs,
-//       fp32 probabilities from exp2f), so that rounding stays far below
-//       fp32 output tolerance even where large scores amplify it.
+//     fp32 path (512-key chunks, up to 4 query heads per workgroup): VGPR
+//       loads, 8 lanes per row for scores and 16 (or 32) lanes per row for
+//       values; the score dot products, chunk max, probability sum and P.V
+//       sums are taken in fp64 (fp32 inputs, fp32 probabilities from exp2f)
+//       and the chunk log-sum-exps stored in fp64, so that rounding stays far
+//       below fp32 output tolerance even where large scores amplify it.  The
+//       fp64 scores of a chunk are kept in LDS, which leaves registers for two
+//       waves per SIMD.
 //     Both paths load the cache with the non-temporal hint: every byte is read
 //     once, and marking its lines evict-first raised the bf16 split kernel
 //     from ~5.6 to ~6.0 TB/s on MI355X (a plain read stream reaches ~6.3 TB/s,
@@ -60,11 +63,12 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = kChunk / kWaves;  // 128
 
 // Bytes of the split-KV partials ([B,Hq,nsplit,d] fp32 outputs, then
-// [B,Hq,nsplit] fp32 log-sum-exps, each padded to 256 bytes) for a chunk size.
-size_t partials_bytes(int B, int Hq, int maxlen, int d, int chunk) {
+// [B,Hq,nsplit] log-sum-exps of lse_bytes each -- fp64 on the fp32 path, fp32
+// on the bf16 path -- each padded to 256 bytes) for a chunk size.
+size_t partials_bytes(int B, int Hq, int maxlen, int d, int chunk, size_t lse_bytes) {
   const size_t nsplit = ((size_t)maxlen + chunk - 1) / chunk;
   const size_t po = (size_t)B * Hq * nsplit * d * sizeof(float);
-  const size_t pl = (size_t)B * Hq * nsplit * sizeof(float);
+  const size_t pl = (size_t)B * Hq * nsplit * lse_bytes;
   return ((po + 255) & ~(size_t)255) + ((pl + 255) & ~(size_t)255);
 }
 
@@ -99,6 +103,12 @@ struct Elem<float> {
   __device__ static inline void store1(float* p, float x) { *p = x; }
 };
 
+// Log-sum-exp of a chunk partial: fp64 on the fp32 path (at |lse| above 128
+// the fp32 half-ulp, 7.6e-6, moves the combine's weights by as much, which a
+// sharp softmax carries into the output), fp32 on the bf16 path.
+template <typename T>
+using LseT = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 __device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, 64); }
 
@@ -106,16 +116,19 @@ __device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xo
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-    const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ seqlens, float* __restrict__ part_o, LseT<T>* __restrict__ part_lse,
     int Hq, int Hkv, int maxlen, int nsplit, float c, float qsign) {
   using E = Elem<T>;
   constexpr int kE = E::kPer16B;            // elements per 16-byte load
-  constexpr int kLaneElems = D / 4;         // score phase: d-range per lane
+  constexpr int kSL = 8;                    // score phase: lanes per row
+  constexpr int kRowSlots = 64 / kSL;       // score phase: rows per wave per pass
+  constexpr int kLaneElems = D / kSL;       // score phase: d-range per lane
   constexpr int kSLoads = kLaneElems / kE;  // 16-byte loads per row per lane
   constexpr int kVLanes = D / kE;           // value phase: lanes per row
   constexpr int kVSlots = 64 / kVLanes;     // rows per wave per pass
   static_assert(64 % kVLanes == 0, "row must split over lanes");
 
+  __shared__ double s_lds[kChunk][GT];  // scores c * (q . k), log2 units
   __shared__ float p_lds[kChunk][GT];
   __shared__ double red_m[kWaves][GT];
   __shared__ double red_l[kWaves][GT];
@@ -140,9 +153,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const T* kp = kc + cbase;
   const T* vp = vc + cbase;
 
-  // ---------------- scores: 4 lanes per row ----------------
-  const int rs = lane >> 2;  // row slot 0..15
-  const int jq = lane & 3;   // quarter of the row
+  // ---------------- scores: kSL lanes per row ----------------
+  const int rs = lane / kSL;  // row slot
+  const int jq = lane % kSL;  // the lane's 16-byte pieces of the row: jq, jq + kSL, ...
   float qv[GT][kLaneElems];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
@@ -151,24 +164,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int cc = 0; cc < kSLoads; ++cc)
 #pragma unroll
       for (int e = 0; e < kE; ++e)
-        qv[g][cc * kE + e] = qsign * E::load1(qrow + cc * (4 * kE) + jq * kE + e);
+        qv[g][cc * kE + e] = qsign * E::load1(qrow + cc * (kSL * kE) + jq * kE + e);
   }
 
-  constexpr int kPasses = kRowsPerWave / 16;  // 8 passes of 16 rows per wave
-  // passes whose loads are issued together (<= 128 VGPRs of loads in flight)
-  constexpr int kSB = (32 / kSLoads) < kPasses ? (32 / kSLoads) : kPasses;
+  constexpr int kPasses = kRowsPerWave / kRowSlots;  // 16 passes of 8 rows per wave
+  // passes whose loads are issued together (64 VGPRs of loads in flight)
+  constexpr int kSB = (16 / kSLoads) < kPasses ? (16 / kSLoads) : kPasses;
   static_assert(kPasses % kSB == 0, "score passes must batch evenly");
-  double sc[kPasses][GT];
+  double mloc[GT];  // running chunk max per head (the same in the kSL lanes of a row)
 #pragma unroll
-  for (int p0 = 0; p0 < kPasses; p0 += kSB) {
+  for (int g = 0; g < GT; ++g) mloc[g] = -INFINITY;
+  // one batch of loads at a time (not unrolled: the scores go to LDS, and an
+  // unrolled loop lets later batches' loads move up and spill), and only the
+  // batches that hold rows of the chunk (wave-uniform)
+  const int wave_rows = min(max(n - wave * kRowsPerWave, 0), kRowsPerWave);
+  const int n_pass = (wave_rows + kRowSlots - 1) / kRowSlots;
+#pragma unroll 1
+  for (int p0 = 0; p0 < n_pass; p0 += kSB) {
     u32x4 buf[kSB][kSLoads];
 #pragma unroll
     for (int i = 0; i < kSB; ++i) {
-      const int row = wave * kRowsPerWave + (p0 + i) * 16 + rs;
+      const int row = wave * kRowsPerWave + (p0 + i) * kRowSlots + rs;
 #pragma unroll
       for (int cc = 0; cc < kSLoads; ++cc) {
         if (row < n)
-          buf[i][cc] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)row * D + cc * (4 * kE) + jq * kE));
+          buf[i][cc] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kp + (size_t)row * D + cc * (kSL * kE) + jq * kE));
         else
           buf[i][cc] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -187,28 +208,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
           for (int g = 0; g < GT; ++g) acc[g] = fma((double)kf[e], (double)qv[g][cc * kE + e], acc[g]);
       }
-      const int row = wave * kRowsPerWave + (p0 + i) * 16 + rs;
+      const int row = wave * kRowsPerWave + (p0 + i) * kRowSlots + rs;
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
         double a = acc[g];
-        a += shfl_xor_d(a, 1);
-        a += shfl_xor_d(a, 2);
-        sc[p0 + i][g] = row < n ? a * (double)c : -INFINITY;
+#pragma unroll
+        for (int m = 1; m < kSL; m <<= 1) a += shfl_xor_d(a, m);
+        const double sv = row < n ? a * (double)c : -INFINITY;
+        mloc[g] = fmax(mloc[g], sv);
+        if (jq == 0) s_lds[row][g] = sv;
       }
     }
   }
 
   // chunk max per head
-  double mloc[GT];
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
-    double mx = -INFINITY;
+    double mx = mloc[g];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) mx = fmax(mx, sc[p][g]);
-    mx = fmax(mx, shfl_xor_d(mx, 4));
-    mx = fmax(mx, shfl_xor_d(mx, 8));
-    mx = fmax(mx, shfl_xor_d(mx, 16));
-    mx = fmax(mx, shfl_xor_d(mx, 32));
+    for (int m = kSL; m < 64; m <<= 1) mx = fmax(mx, shfl_xor_d(mx, m));
     mloc[g] = mx;
   }
   if (lane == 0) {
@@ -224,25 +242,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int w = 1; w < kWaves; ++w) mx = fmax(mx, red_m[w][g]);
     M[g] = mx;  // finite: the chunk has at least one row
   }
-  // probabilities to LDS, partial sums
+  // probabilities to LDS, partial sums: each lane takes rows lane and
+  // lane + 64 of its wave's (rows past the length give 0; their scores were
+  // written only up to the end of their batch)
   double lpart[GT];
 #pragma unroll
   for (int g = 0; g < GT; ++g) lpart[g] = 0.0;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = wave * kRowsPerWave + p * 16 + rs;
+  for (int i = 0; i < kRowsPerWave / 64; ++i) {
+    const int row = wave * kRowsPerWave + i * 64 + lane;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-      const float e = exp2f((float)(sc[p][g] - M[g]));
-      if (jq == 0) {
-        p_lds[row][g] = e;
-        lpart[g] += e;
-      }
+      const float e = row < n ? exp2f((float)(s_lds[row][g] - M[g])) : 0.f;
+      p_lds[row][g] = e;
+      lpart[g] += e;
     }
   }
 #pragma unroll
   for (int g = 0; g < GT; ++g) {
     double s = lpart[g];
+    s += shfl_xor_d(s, 1);
+    s += shfl_xor_d(s, 2);
     s += shfl_xor_d(s, 4);
     s += shfl_xor_d(s, 8);
     s += shfl_xor_d(s, 16);
@@ -316,7 +336,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
     const size_t pidx = ((size_t)b * Hq + h0 + g) * nsplit + split;
     part_o[pidx * D + d] = (float)(a / l);
-    if (d == 0) part_lse[pidx] = (float)(M[g] * 0.6931471805599453 + log(l));
+    if (d == 0) part_lse[pidx] = (LseT<T>)(M[g] * 0.6931471805599453 + log(l));
   }
 }
 
@@ -331,11 +351,13 @@ constexpr int kCombBatch = 1024;  // weights staged in LDS per batch
 
 template <typename T, int D>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const float* __restrict__ part_o, const LseT<T>* __restrict__ part_lse,
     const int32_t* __restrict__ seqlens, T* __restrict__ o, int Hq, int maxlen, int nsplit, int chunk) {
   using E = Elem<T>;
+  using L_ = LseT<T>;
   constexpr int NG = kCombThreads / D;  // split groups
   __shared__ float w_lds[kCombBatch];
+  __shared__ L_ red_mx[kCombThreads / 64];
   __shared__ float red[kCombThreads / 64];
   __shared__ float acc_lds[NG][D];
   const int tid = threadIdx.x;
@@ -349,19 +371,19 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     return;
   }
   const size_t base = ((size_t)b * Hq + h) * nsplit;
-  const float* lse = part_lse + base;
+  const L_* lse = part_lse + base;
   const float* po = part_o + base * D;
 
   // block max of the log-sum-exps
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += kCombThreads) mx = fmaxf(mx, lse[s]);
+  L_ mx = -INFINITY;
+  for (int s = tid; s < ns; s += kCombThreads) mx = fmax(mx, lse[s]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wave] = mx;
+  for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, (L_)__shfl_xor(mx, off, 64));
+  if (lane == 0) red_mx[wave] = mx;
   __syncthreads();
-  mx = red[0];
+  mx = red_mx[0];
 #pragma unroll
-  for (int w = 1; w < kCombThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+  for (int w = 1; w < kCombThreads / 64; ++w) mx = fmax(mx, red_mx[w]);
 
   const int d = tid % D, sg = tid / D;
   float acc = 0.f, wpart = 0.f;
@@ -369,9 +391,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const int nb = min(kCombBatch, ns - s0);
     __syncthreads();  // previous batch's weights fully read (and red[] read above)
     for (int i = tid; i < nb; i += kCombThreads) {
-      // the fp32 path takes the accurate exponential (about 1 ulp), bf16 the fast
-      // one, whose error grows with |argument|
-      const float w = std::is_same<T, float>::value ? expf(lse[s0 + i] - mx) : __expf(lse[s0 + i] - mx);
+      // the fp32 path takes the fp64 exponential of the fp64 difference, bf16
+      // the fast one, whose error grows with |argument|
+      float w;
+      if constexpr (std::is_same<T, float>::value) w = (float)exp(lse[s0 + i] - mx);
+      else w = __expf(lse[s0 + i] - mx);
       w_lds[i] = w;
       wpart += w;
     }
@@ -702,7 +726,7 @@ template <int D, bool PAGED>
 hipError_t launch_bf16_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int gm = bf16_group_tile(a.Hq / a.Hkv);
   const int chunk = bf16_decode_chunk(a.B, a.Hq, a.Hkv, a.maxlen);
-  if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk) > a.ws_bytes) return hipErrorInvalidValue;
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, chunk, sizeof(float)) > a.ws_bytes) return hipErrorInvalidValue;
   const int nsplit = (a.maxlen + chunk - 1) / chunk;
   const int G = a.Hq / a.Hkv;
   float* part_o = static_cast<float*>(a.ws);
@@ -728,12 +752,12 @@ hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if (partials_bytes(a.B, a.Hq, a.maxlen, D, kChunk) > a.ws_bytes) return hipErrorInvalidValue;
+  if (partials_bytes(a.B, a.Hq, a.maxlen, D, kChunk, sizeof(LseT<T>)) > a.ws_bytes) return hipErrorInvalidValue;
   const int nsplit = (a.maxlen + kChunk - 1) / kChunk;
   const int G = a.Hq / a.Hkv;
   float* part_o = static_cast<float*>(a.ws);
   const size_t po_bytes = (size_t)a.B * a.Hq * nsplit * D * sizeof(float);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
+  LseT<T>* part_lse = reinterpret_cast<LseT<T>*>(static_cast<char*>(a.ws) + ((po_bytes + 255) & ~(size_t)255));
   dim3 g1(nsplit, a.Hkv * (G / GT), a.B);
   if (g1.y > 65535u || g1.z > 65535u) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_split_kernel<T, D, GT>), g1, dim3(256), 0, stream, static_cast<const T*>(a.q),
@@ -746,15 +770,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Heads per block: 4 at d = 64; at d = 128 the fp32 query slices of 4 heads
-// (128 VGPRs) beside their fp64 scores and the loads in flight would spill,
-// so 2.
 template <typename T, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  if constexpr (D <= 64) {
-    if (G % 4 == 0) return launch_t<T, D, 4>(a, stream);
-  }
+  if (G % 4 == 0) return launch_t<T, D, 4>(a, stream);
   if (G % 2 == 0) return launch_t<T, D, 2>(a, stream);
   return launch_t<T, D, 1>(a, stream);
 }
@@ -763,8 +782,8 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
   // large enough for either path's chunking
-  const size_t a = partials_bytes(B, Hq, maxlen, d, kChunk);
-  const size_t b = partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen));
+  const size_t a = partials_bytes(B, Hq, maxlen, d, kChunk, sizeof(double));
+  const size_t b = partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen), sizeof(float));
   return a > b ? a : b;
 }
 
@@ -789,7 +808,7 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
 }
 
 size_t decode_noalloc_bytes(int B, int Hq, int Hkv, int maxlen, int d) {
-  return partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen));
+  return partials_bytes(B, Hq, maxlen, d, bf16_decode_chunk(B, Hq, Hkv, maxlen), sizeof(float));
 }
 
 }  // namespace fa

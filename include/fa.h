@@ -191,8 +191,9 @@ int fa_decode_ws(const void* q, const void* kcache, const void* vcache,
 
 /* Decode with fp32 q/caches/o (same layouts and semantics).  Scores, chunk
  * maxima, sums and P.V accumulate in fp64 over fp32 inputs; probabilities,
- * stored partials and the output are fp32: within about 1e-5 of the exact
- * result for unit-scale caches. */
+ * the chunks' partial outputs and the output are fp32, their log-sum-exps
+ * fp64 (so the merge weights stay exact when |lse| is large): within about
+ * 1e-5 of the exact result for unit-scale caches. */
 int fa_decode_f32(const float* q, const float* kcache, const float* vcache,
                   const int32_t* seqlens, float* o, int B, int Hq, int Hkv,
                   int maxlen, int d, float scale, void* stream);

@@ -152,10 +152,11 @@ def test_decode_ws_rejects_small_or_missing_workspace(name):
 @needs_lib
 def test_workspace_bytes():
     lib = binding.load_library()
-    # two fp32 partial arrays: [B,Hq,nsplit,d] and [B,Hq,nsplit], each padded to 256 bytes
+    # the fp32 path's partials, the larger of the two paths' here: [B,Hq,nsplit,d]
+    # fp32 outputs and [B,Hq,nsplit] fp64 log-sum-exps, each padded to 256 bytes
     nsplit = (32768 + 511) // 512
     po = 64 * 32 * nsplit * 128 * 4
-    pl = 64 * 32 * nsplit * 4
+    pl = 64 * 32 * nsplit * 8
     rnd = lambda x: (x + 255) // 256 * 256
     assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 128) == rnd(po) + rnd(pl)
     assert lib.fa_decode_workspace_bytes(0, 32, 8, 32768, 128) == 0

@@ -316,6 +316,22 @@ def test_decode_f32_sharp_scores(kind, lens, d, G, scale):
     check_close(o, ro, F32_MAX_ABS, f"decode f32 {kind}")
 
 
+def test_decode_f32_merge_at_large_lse():
+    """Sharp scores (q and K scaled by 4, scale 0.35, d = 64) over several
+    512-key chunks, with chunk log-sum-exps up to ~200, where fp32's half-ulp
+    (7.6e-6 above 128) shifts the merge weights.  On these inputs a model with
+    exact chunk partials merged through fp32-stored log-sum-exps is off by
+    1.02e-5 -- past the fp32 bar on its own -- and by ~1e-7 with fp64 ones."""
+    lens, d, G, scale = [3471, 535, 5166], 64, 8, float(np.float32(0.35))
+    q, kc, vc, ls, _ = I.decode_inputs(len(lens), 2 * G, 2, d, 1, max(lens), max(lens), "f32", seed=3,
+                                       seqlens=lens)
+    q, kc = q * 4, kc * 4
+    o = gpu_decode(q, kc, vc, ls, scale)
+    ro, rl = oracle.decode(q, kc, vc, ls, scale)
+    assert np.nanmax(rl) > 128
+    check_close(o, ro, F32_MAX_ABS, "decode f32 large lse")
+
+
 def test_decode_matches_last_prefill_row():
     """Decode of token i against K,V[0..i] equals causal prefill row i (both on the GPU)."""
     q, k, v, scale = I.prefill_inputs(2, 8, 2, 700, 128, "bf16", seed=23)

@@ -8,9 +8,9 @@
 // During Local Inference?", "Kernel Fusion Keeps More of the Attention Chain
 // in One Execution Path").
 //
-// Layout: a workgroup takes 16 query rows of one head; each of its 4 or 8
+// Layout: a workgroup takes 16 query rows of one head; each of its 4, 8 or 16
 // waves covers all 16 rows (4 lanes per row, each lane a quarter of d in
-// interleaved 16-byte pieces) and takes every 4th (8th) 8-key batch of the keys,
+// interleaved 16-byte pieces) and takes every 4th (8th, 16th) 8-key batch of the keys,
 // keeping its own running max, sum and output for the rows.  q and the output
 // accumulator stay in registers (fp64); K and V rows come straight from
 // memory, the 16 rows of a wave reading the same 16-byte pieces.  The
@@ -38,10 +38,11 @@ namespace {
 constexpr int kF32Rows = kPrefillF32Rows;  // query rows per workgroup
 constexpr int kF32Batch = 8;   // keys per batch (one max and one rescale per batch)
 // Waves per workgroup (SPLIT), each taking every SPLIT-th key batch: 8 while
-// the grid is small (one head of 256 rows: 57 -> 36 us on MI355X), 4 for
-// large grids, where at d = 128 the 8-wave form fits only one workgroup per
-// CU (3-7% slower there).
+// the grid is small (one head of 256 rows: 57 -> 36 us on MI355X), 16 for the
+// smallest d = 64 grids, 4 for large grids, where at d = 128 the 8-wave form
+// fits only one workgroup per CU (3-7% slower there).
 constexpr int kF32SmallGrid = 4096;  // workgroups below which 8 waves are used
+constexpr int kF32TinyGrid = 1024;   // d = 64: workgroups below which 16 waves are used
 
 __device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, 64); }
 
@@ -196,6 +197,10 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const int BH = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * BH;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if constexpr (D == 64) {
+    // at d = 64 sixteen waves fit a CU (128 VGPRs, a 132 KB merge buffer)
+    if (blocks < kF32TinyGrid) return launch_split<D, CAUSAL, 16>(a, stream, n_qtiles, BH, (unsigned)blocks);
+  }
   return blocks < kF32SmallGrid ? launch_split<D, CAUSAL, 8>(a, stream, n_qtiles, BH, (unsigned)blocks)
                                 : launch_split<D, CAUSAL, 4>(a, stream, n_qtiles, BH, (unsigned)blocks);
 }

@@ -62,12 +62,14 @@ def test_fp32_prefill_shapes(N, d, causal):
     check_close(lse, rl, F32_LSE_MAX_ABS, "lse")
 
 
-@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
-def test_fp32_prefill_large_grid(d, causal):
-    """64 heads x 64 sixteen-row tiles = 4096 workgroups: the launch that takes
-    four waves per workgroup (the smaller grids above take eight), with a
-    ragged last tile."""
-    q, k, v, scale = I.prefill_inputs(1, 64, 8, 1020, d, "f32", seed=d)
+@pytest.mark.parametrize("d,causal,Hq,Hkv,N", [(64, True, 64, 8, 1020), (128, False, 64, 8, 1020),
+                                               (64, False, 16, 4, 2000)])
+def test_fp32_prefill_large_grid(d, causal, Hq, Hkv, N):
+    """The launch forms past the small grids above (which take 16 waves per
+    workgroup at d = 64, 8 at d = 128): 64 heads x 64 sixteen-row tiles = 4096
+    workgroups take 4 waves, 16 heads x 125 tiles = 2000 workgroups at d = 64
+    take 8; ragged last tiles."""
+    q, k, v, scale = I.prefill_inputs(1, Hq, Hkv, N, d, "f32", seed=d + N)
     o, lse = gpu_prefill(q, k, v, causal, scale)
     ro, rl = oracle.attention(q, k, v, causal, scale)
     check_close(o, ro, F32_MAX_ABS, "o")

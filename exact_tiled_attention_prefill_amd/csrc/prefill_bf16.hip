@@ -34,9 +34,13 @@
 //     be permuted freely as long as V^T uses the same order), so P never
 //     touches LDS, and O^T keeps each query's output in its own lane.
 //   * K and V tiles (64 keys) are copied HBM -> LDS by global_load_lds_dwordx4
-//     (no VGPR staging) into a two-slot ring: K of the tile after next and V
-//     of the next tile stream in while the current ones are read.  The
-//     workgroup barrier between tiles does not drain in-flight DMA.  K is read
+//     (no VGPR staging) into a ring: with four waves two slots (K of the tile
+//     after next and V of the next tile stream in while the current ones are
+//     read; a workgroup barrier after every tile), with eight waves four slots
+//     (a barrier after every second tile; the copies of a step are issued by
+//     one half of the waves, alternating, so one wave of every SIMD keeps the
+//     matrix cores busy while the other issues copies).  The barrier does not
+//     drain in-flight DMA.  K is read
 //     with ds_read_b128, V with the gfx950 transposing ds_read_b64_tr_b16
 //     straight into the MFMA A operand layout.  16-byte chunks are
 //     XOR-swizzled by row so both reads are bank-conflict free; the DMA source
@@ -51,7 +55,8 @@
 //     row max grows by more than 2^8; otherwise exponents are taken against
 //     the stale max (p <= 256; exact after the final division by l).
 //   * Causal: tiles above the diagonal are never loaded; masks run only on
-//     diagonal, ragged and window tiles.
+//     diagonal, ragged and window tiles.  Under a sliding window every query
+//     tile sees about the same number of keys, so its tiles are not paired.
 //   * Scheduling: workgroup ids are dealt round-robin to the 8 XCDs, so each
 //     XCD is given a contiguous range of work items; within it the items are
 //     ordered (block of KV head groups, slot, group, query head of the group),
@@ -80,6 +85,22 @@ namespace {
 #endif
 #ifndef FA_PREFILL_BC
 #define FA_PREFILL_BC 64
+#endif
+// K/V ring slots of the eight-wave kernel (2 or 4; 4 takes one workgroup
+// barrier per two key tiles instead of one per tile).
+#ifndef FA_PREFILL_RING8
+#define FA_PREFILL_RING8 4
+#endif
+static_assert(FA_PREFILL_RING8 == 2 || FA_PREFILL_RING8 == 4, "ring slots: 2 or 4");
+// Causal packed sequences under a window: pair query tiles as without one (1)
+// or run one tile per slot (0).
+#ifndef FA_WINDOW_PAIR
+#define FA_WINDOW_PAIR 0
+#endif
+// With four slots, half of the waves copy the tiles of each step (1), or all
+// of them (0).
+#ifndef FA_PREFILL_HALFCOPY
+#define FA_PREFILL_HALFCOPY 1
 #endif
 static_assert(FA_PREFILL_WAVES == 0 || FA_PREFILL_WAVES == 4 || FA_PREFILL_WAVES == 8, "waves: 0 (choose), 4 or 8");
 constexpr int kBC = FA_PREFILL_BC;     // keys per tile (64, or 32)
@@ -152,12 +173,30 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   constexpr int MD = D / 32;                // 32-row blocks of O^T
   constexpr int RC = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = kBC * D * 2;         // bytes per K (or V) tile
-  constexpr int CPT = kBC * RC / kThreads;  // DMA chunks per thread per K (or V) tile
-  static_assert(CPT * kThreads == kBC * RC, "tile must split evenly");
-  // Two ring slots of K and V tiles: ring[slot][0] = K, ring[slot][1] = V.
+  // Ring of K and V tiles; tile t lives in slot t % kRing.  Four-wave
+  // workgroups (two per CU) keep two slots and take the workgroup barrier
+  // after every tile; eight-wave workgroups (one per CU) keep four slots and
+  // take it after every second tile (+0.5 to +1.3% on long rows), except the
+  // non-causal packed kernel, whose tile loop spills registers with four.
   // The DMA into the ring is inline asm, so the compiler does not track it;
   // ordering is explicit (vmcnt + lgkmcnt + barrier).
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[2][2][TILE];
+  constexpr int kRing = (kWaves == 8 && (CAUSAL || !VARLEN)) ? FA_PREFILL_RING8 : 2;
+  constexpr int kPer = kRing / 2;  // tiles per barrier
+  // Waves that copy a tile: all of them, or (four slots) one half per step,
+  // waves 0-3 in even steps and 4-7 in odd ones, so that one wave of every
+  // SIMD runs its matrix products while the other issues copies.
+  constexpr int kCopyWaves = (kRing == 4 && FA_PREFILL_HALFCOPY) ? kWaves / 2 : kWaves;
+  constexpr int kCopyThreads = 64 * kCopyWaves;
+  constexpr int CPT = kBC * RC / kCopyThreads;  // DMA chunks per copying thread per K (or V) tile
+  static_assert(CPT * kCopyThreads == kBC * RC, "tile must split evenly");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * 2 * TILE];
+  // Byte offsets of slot s's K and V tiles.  Two slots: (K, V) pairs.  Four
+  // slots: the K tiles, then the V tiles, so that every K read and (with the
+  // V region's base in the lane's V offsets) every V read stays within the
+  // 16-bit immediate offset of ds_read.
+  constexpr auto kslot = [](int sl) { return kRing == 2 ? 2 * sl * TILE : sl * TILE; };
+  constexpr auto vslot = [](int sl) { return kRing == 2 ? (2 * sl + 1) * TILE : (kRing + sl) * TILE; };
+  constexpr auto vread = [](int sl) { return kRing == 2 ? (2 * sl + 1) * TILE : sl * TILE; };
 
   const int wave = (int)threadIdx.x >> 6;
 
@@ -168,7 +207,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
   const int G = Hq / Hkv;
   // causal: slot s of a head runs query tiles n-1-s and s (equal work per slot)
-  const int n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  // Causal tiles are paired (below) unless a window gives every query tile
+  // about the same number of keys.
+  const bool pair = CAUSAL && !(VARLEN && !FA_WINDOW_PAIR && vr.window >= 0);
+  const int n_slots = pair ? (n_qtiles + 1) / 2 : n_qtiles;
   const int n_groups = n_items / (n_slots * G);  // B * Hkv
   const int BG = G >= block_heads ? 1 : (block_heads + G - 1) / G;  // KV groups per block
   const int per_block = BG * G * n_slots;
@@ -209,13 +251,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   // s), so every workgroup streams about the same number of key tiles and the
   // XCDs do not finish on a tail of long workgroups.
   const int n_qt = VARLEN ? (Lq + kBR - 1) / kBR : n_qtiles;  // this sequence's query tiles
-  const int n_pass = CAUSAL ? 2 : 1;
+  const int n_pass = pair ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
-  const int qtile = !CAUSAL ? tslot : (pass == 0 ? n_qt - 1 - tslot : tslot);
+  const int qtile = !pair ? tslot : (pass == 0 ? n_qt - 1 - tslot : tslot);
   // pass 1 only when the mirror is a different tile; past a shorter
   // sequence's tiles the whole workgroup skips the pass
-  if (CAUSAL && (tslot > n_qt - 1 - tslot || (pass == 1 && tslot == n_qt - 1 - tslot))) continue;
-  if (VARLEN && !CAUSAL && tslot >= n_qt) continue;
+  if (pair && (tslot > n_qt - 1 - tslot || (pass == 1 && tslot == n_qt - 1 - tslot))) continue;
+  if (VARLEN && !pair && tslot >= n_qt) continue;
 
   // Every lane-dependent value of the pass derives from the lane id taken
   // here (mbcnt, in volatile asm so that it is not hoisted), so the compiler
@@ -253,20 +295,25 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   for (int ks = 0; ks < KS; ++ks) koff[ks] = xp * (D * 2) + (((2 * ks + hp) ^ k_swz<D>(xp)) << 4);
   int voff[MD];  // V^T fragments: row 4hi + (i>>2) (+16ks2 + 8half), chunk of column md*32 + ...
   {
+    // four slots: the V region's base, kept opaque so that it stays in the
+    // offsets instead of being folded into the reads' immediates
+    int vbase = kRing == 2 ? 0 : kRing * TILE;
+    if constexpr (kRing != 2) asm volatile("" : "+v"(vbase));
     const int i = lp & 15;
     const int row = 4 * hp + (i >> 2);
     const int colc = 2 * ((lp >> 4) & 1) + ((i & 3) >> 1);  // chunk within the 32-column block
 #pragma unroll
     for (int md = 0; md < MD; ++md)
-      voff[md] = row * (D * 2) + (((4 * md + colc) ^ v_swz<D>(row)) << 4) + 8 * (i & 1);
+      voff[md] = vbase + row * (D * 2) + (((4 * md + colc) ^ v_swz<D>(row)) << 4) + 8 * (i & 1);
   }
 
-  // ---- DMA: chunk p = i*kThreads + wave*64 + lane of the tile; byte offsets within the tile ----
+  // ---- DMA: chunk p = i*kCopyThreads + cw*64 + lane of the tile; byte offsets within the tile ----
   // rows of chunk i are dma_row + i*kRowStep; the swizzle depends on the row
   // only modulo 16, so one offset serves every chunk of a lane
-  constexpr int kRowStep = kThreads / RC;
+  constexpr int kRowStep = kCopyThreads / RC;
   static_assert(kRowStep % 16 == 0, "row step keeps the swizzle");
-  const int dma_row = (wave_s * 64 + lp) / RC;
+  const int cw = wave_s % kCopyWaves;  // the wave's place among the copying waves
+  const int dma_row = (cw * 64 + lp) / RC;
   const int dma_cp = lp % RC;
   const uint32_t dk_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ k_swz<D>(dma_row)) << 4));
   const uint32_t dv_off = (uint32_t)(dma_row * kv_rs * 2 + ((dma_cp ^ v_swz<D>(dma_row)) << 4));
@@ -281,6 +328,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
   const int t_begin = W >= 0 ? max(0, q0 + off - W) / kBC : 0;
   const int ntiles = max((max(kv_end, 0) + kBC - 1) / kBC - t_begin, 0);
 
+  // Does this wave copy the tiles of a step of parity p (wave-uniform)?
+  auto copies_of = [&](int p) { return kCopyWaves == kWaves || wave_s / kCopyWaves == p; };
   // Copy rows [k0, k0+64) of the K (IS_K) or V head slab into an LDS tile.
   // Rows past the end re-read the last row (finite values whose scores are
   // masked).
@@ -291,15 +340,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     const uint32_t doff = IS_K ? dk_off : dv_off;
     if (k0 + kBC <= Lk) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        dma16(base + (size_t)i * kRowStep * kv_rs * 2, doff, lds + (i * kThreads + wave_s * 64) * 16);
+      for (int i = 0; i < CPT; ++i) {
+        // half-wave copies: one scalar base per tile and the chunk's row
+        // step in the lane offset, which keeps the copy bases out of the
+        // SGPRs the compiler would otherwise spill to VGPR lanes
+        if constexpr (kCopyWaves < kWaves)
+          dma16(base, doff + (uint32_t)(i * kRowStep * kv_rs * 2), lds + (i * kCopyThreads + cw * 64) * 16);
+        else
+          dma16(base + (size_t)i * kRowStep * kv_rs * 2, doff, lds + (i * kCopyThreads + cw * 64) * 16);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         // offset from the tile base: the clamped row is >= 0, so the unsigned
         // 32-bit offset never wraps
         const int r = min(dma_row + i * kRowStep, Lk - 1 - k0);
-        dma16(base, doff + (r - dma_row) * kv_rs * 2, lds + (i * kThreads + wave_s * 64) * 16);
+        dma16(base, doff + (r - dma_row) * kv_rs * 2, lds + (i * kCopyThreads + cw * 64) * 16);
       }
     }
   };
@@ -376,10 +432,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
 
   auto iter = [&](int t, f32x16 (&sc)[kMB], f32x16 (&sn)[kMB], float& mx_c, float& mx_n, auto slot_c,
                   auto full_c) {
-    constexpr int SL = decltype(slot_c)::value;
+    constexpr int SL = decltype(slot_c)::value;     // t % kRing
     constexpr bool FULL = decltype(full_c)::value;  // tile t+1 exists
-    if (t + 2 < ntiles) issue_half(t + 2, std::true_type{}, ring[SL][0]);
-    if (t + 1 < ntiles) issue_half(t + 1, std::false_type{}, ring[SL ^ 1][1]);
+    // the barrier closes every kPer-th step and the last one (four slots:
+    // after the loop)
+    constexpr bool BAR = SL % kPer == kPer - 1 || !FULL;
+    // K runs kPer + 1 tiles ahead, V kPer tiles: their slots were last read
+    // before the previous barrier
+    if (copies_of(SL & 1)) {
+      if (t + kPer + 1 < ntiles) issue_half(t + kPer + 1, std::true_type{}, ring + kslot((SL + kPer + 1) % kRing));
+      if (t + kPer < ntiles) issue_half(t + kPer, std::false_type{}, ring + vslot((SL + kPer) % kRing));
+    }
     // lazy rescale against tile t's row max
     {
       const float mxs = mx_c * c;  // -inf stays -inf (c > 0)
@@ -395,7 +458,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     }
     const float negm = (VARLEN && m_run == -INFINITY) ? 0.f : -m_run;
     // ---- region A: scores of tile t+1 || probabilities of tile t ----
-    if constexpr (FULL) scores(sn, ring[SL ^ 1][0]);
+    if constexpr (FULL) scores(sn, ring + kslot((SL + 1) % kRing));
     bf16x8 pf[kBC / 16];
     {
       float lsum[2] = {0.f, 0.f};
@@ -434,7 +497,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
       if (needs_mask(k1)) mask_scores(sn, k1);
     }
     // ---- region B: O^T += V^T P^T for tile t || row max of tile t+1 ----
-    const uint8_t* vl = ring[SL][1];
+    const uint8_t* vl = ring + vread(SL);
 #pragma unroll
     for (int ks2 = 0; ks2 < kBC / 16; ++ks2)
 #pragma unroll
@@ -454,33 +517,66 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         if (i + 2 < MD * kBC / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
-    if (t + 1 < ntiles) wait_vmem_le<0>();
-    lds_reads_done();
-    ring_barrier();
+    if constexpr (BAR) {
+      if (t + 1 < ntiles) wait_vmem_le<0>();
+      lds_reads_done();
+      ring_barrier();
+    }
   };
 
   if (ntiles > 0) {
-    // prologue: K(0), V(0) and K(1) in flight; scores and row max of tile 0
-    issue_half(0, std::true_type{}, ring[0][0]);
-    issue_half(0, std::false_type{}, ring[0][1]);
-    if (ntiles > 1) issue_half(1, std::true_type{}, ring[1][0]);
+    // prologue: K(0..kPer) and V(0..kPer-1) in flight; scores and row max of tile 0
+    if (copies_of(0)) {
+      issue_half(0, std::true_type{}, ring + kslot(0));
+      issue_half(0, std::false_type{}, ring + vslot(0));
+    }
+    if (copies_of(1) && ntiles > 1) issue_half(1, std::true_type{}, ring + kslot(1));
+    if constexpr (kPer == 2) {
+      if (copies_of(1) && ntiles > 1) issue_half(1, std::false_type{}, ring + vslot(1));
+      if (copies_of(0) && ntiles > 2) issue_half(2, std::true_type{}, ring + kslot(2));
+    }
     wait_vmem_le<0>();
     ring_barrier();
-    scores(sA, ring[0][0]);
+    scores(sA, ring + kslot(0));
     if (needs_mask(t_begin * kBC)) mask_scores(sA, t_begin * kBC);
     mxA = rowmax(sA);
     lds_reads_done();
-    ring_barrier();  // K(0)'s slot is refilled by iteration 0
+    ring_barrier();  // K(0)'s slot is refilled by the first steps
+    // unrolled by kRing: ring slots are immediates in every LDS access
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
     int t = 0;
-    for (; t + 2 < ntiles; t += 2) {
-      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::true_type{});
-      iter(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{}, std::true_type{});
-    }
-    if (t + 1 < ntiles) {
-      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::true_type{});
-      iter(t + 1, sB, sA, mxB, mxA, std::integral_constant<int, 1>{}, std::false_type{});
+    if constexpr (kRing == 2) {
+      for (; t + 2 < ntiles; t += 2) {
+        iter(t, sA, sB, mxA, mxB, I0{}, T_{});
+        iter(t + 1, sB, sA, mxB, mxA, I1{}, T_{});
+      }
+      if (t + 1 < ntiles) {
+        iter(t, sA, sB, mxA, mxB, I0{}, T_{});
+        iter(t + 1, sB, sA, mxB, mxA, I1{}, F_{});
+      } else {
+        iter(t, sA, sB, mxA, mxB, I0{}, F_{});
+      }
     } else {
-      iter(t, sA, sB, mxA, mxB, std::integral_constant<int, 0>{}, std::false_type{});
+      // Four slots: the last step also computes the scores of the slot after
+      // it (stale keys no copy is writing), which nothing uses; one code copy
+      // per slot serves every tile count.
+      for (; t < ntiles; t += 4) {
+        iter(t, sA, sB, mxA, mxB, I0{}, T_{});
+        if (t + 1 >= ntiles) break;
+        iter(t + 1, sB, sA, mxB, mxA, I1{}, T_{});
+        if (t + 2 >= ntiles) break;
+        iter(t + 2, sA, sB, mxA, mxB, I2{}, T_{});
+        if (t + 3 >= ntiles) break;
+        iter(t + 3, sB, sA, mxB, mxA, I3{}, T_{});
+      }
+      // no copy is in flight after the last step
+      lds_reads_done();
+      ring_barrier();
     }
   }
 
@@ -510,7 +606,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
     if (lse != nullptr && he == 0) {
-      const float lv = empty ? -INFINITY : m_run * kLn2 + __logf(lt);
+      // one rounding (fma), whatever the surrounding code
+      const float lv = empty ? -INFINITY : fmaf(m_run, kLn2, __logf(lt));
       if (VARLEN)
         lse[(size_t)h * vr.total_q + qstart + row_e] = lv;
       else
@@ -532,7 +629,9 @@ template <int D, bool CAUSAL, bool VARLEN, int WAVES>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kBR = 32 * WAVES;  // query rows per workgroup
   const int n_qtiles = (a.N + kBR - 1) / kBR;
-  const int n_slots = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // causal slots pair two query tiles
+  // causal slots pair two query tiles, except under a window (as in the kernel)
+  const bool pair = CAUSAL && !(VARLEN && !FA_WINDOW_PAIR && a.varlen.window >= 0);
+  const int n_slots = pair ? (n_qtiles + 1) / 2 : n_qtiles;
   const long long items = (long long)n_slots * a.B * a.Hq;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int block_heads = block_heads_for(n_slots);

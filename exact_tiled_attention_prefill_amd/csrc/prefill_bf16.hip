@@ -21,7 +21,7 @@
 //   * Workgroup = 4 waves = 128 query rows of one head; two workgroups share
 //     a CU, so every SIMD runs two waves from different workgroups whose
 //     softmax (VALU) and matrix products (MFMA) interleave.  Rows that see
-//     8K keys or more on average use 8 waves = 256 rows instead (one
+//     4K keys or more on average use 8 waves = 256 rows instead (one
 //     workgroup per CU, half the K/V copies per row).  Wave w of W owns rows
 //     q0 + w + Wj (j = 0..31): interleaving the rows gives every wave the
 //     same causal work, so the per-tile barrier never waits on a wave with
@@ -74,10 +74,10 @@ namespace {
 
 // Launch shape: waves per workgroup (a template parameter, 4 or 8) and keys
 // per tile (compile-time).  Eight waves (256 query rows sharing each K/V
-// tile, one workgroup per CU) halve the L2 -> LDS traffic and gain 1-3% when
-// the average query row sees 8K keys or more, but lose 3-11% on shorter rows
-// (causal 1K-8K, 1K-key windows), where one workgroup per CU leaves its
-// prologue and the wider causal diagonal exposed.  The launcher picks the
+// tile, one workgroup per CU, four ring slots) halve the L2 -> LDS traffic
+// and gain ~2% when the average query row sees 4K keys or more, but lose
+// 2-20% on shorter rows (causal 2K-4K, 1K-key windows), where one workgroup
+// per CU leaves its prologue and the wider causal diagonal exposed.  The launcher picks the
 // width per call (FA_PREFILL_WAVES=4 or 8 forces one, for testing).  32-key
 // tiles are ~3% slower.
 #ifndef FA_PREFILL_WAVES
@@ -167,7 +167,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void prefill_bf16_kernel(
     int Hq, int Hkv, int N, int n_qtiles, int n_items, int block_heads, float c, uint32_t qflip,
     VarlenRef vr) {
   constexpr int kWaves = WAVES;
-  constexpr int kThreads = 64 * kWaves;
   constexpr int kBR = 32 * kWaves;          // query rows per workgroup
   constexpr int KS = D / 16;                // k-steps of S^T = K Q^T
   constexpr int MD = D / 32;                // 32-row blocks of O^T
@@ -643,7 +642,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Eight waves when the average query row sees at least 8192 keys (d = 128;
+// Eight waves when the average query row sees at least 4096 keys (d = 128;
 // the wider workgroup was measured there only).  Dense rows see N keys, or
 // (N + 1) / 2 on average under the causal mask.  Packed sequences of average
 // lengths Lq = total_q / B, Lk = total_k / B see Lk keys, or Lk - (Lq - 1) / 2
@@ -660,7 +659,7 @@ bool wide_launch(const PrefillArgs& a) {
   } else {
     keys = a.causal ? 0.5 * ((double)a.N + 1) : (double)a.N;
   }
-  return keys >= 8192.0;
+  return keys >= 4096.0;
 }
 
 template <int D, bool VARLEN>

@@ -1,6 +1,6 @@
 """GPU parity for the 8-wave prefill launch (256 query rows per workgroup).
 
-The launcher uses it when the average query row sees 8192 keys or more
+The launcher uses it when the average query row sees 4096 keys or more
 (d = 128).  These cases are chosen to take it, with ragged query and key ends
 (lengths that are not multiples of the 256-row or 64-key tiles), and are
 checked on sampled rows against the fp64 oracle to the bf16 bar.
@@ -44,6 +44,13 @@ def test_wide_dense_causal_gqa_ragged():
     8231 keys on average; the paired query tiles include the ragged last one."""
     N = 16461
     _dense(1, 4, 1, N, True, 62, [0, 1, 255, 256, 511, 8000, 8230, 16383, 16384, N - 2, N - 1])
+
+
+def test_wide_dense_causal_mha_near_threshold():
+    """Causal MHA, N = 8300: rows see 4150.5 keys on average, just above the
+    width threshold; ragged last query and key tiles."""
+    N = 8300
+    _dense(1, 2, 2, N, True, 65, [0, 1, 63, 64, 255, 256, 4095, 4096, 8191, 8192, N - 1])
 
 
 @pytest.mark.parametrize("causal", [True, False])

@@ -73,6 +73,29 @@ def test_wide_varlen_long_prefixes(causal):
     assert err <= BF16_LSE_MAX_ABS, f"wide varlen lse max-abs {err:.3e}"
 
 
+@pytest.mark.parametrize("causal,window", [(True, -1), (True, 4500), (False, -1), (False, 4500)])
+def test_wide_varlen_short_sequences_and_window(causal, window):
+    """Eight-wave launch (the batch's rows see >= 4096 keys on average) over
+    sequences from 1 to 200 keys beside long ones: key-tile counts 1 to 4
+    take every remaining-tile path of the four-slot ring; with a 4500-key
+    window the long rows start past key 0."""
+    print(f"wide varlen short+long causal={causal} window={window}", flush=True)
+    lens = [(1, 1), (2, 2), (63, 63), (64, 64), (65, 65), (130, 130), (200, 200), (1, 150),
+            (500, 20000), (300, 18000), (257, 16000)]
+    q, k, v, cu_q, cu_k, scale = I.varlen_inputs(lens, 4, 2, 128, seed=66 + causal + 2 * (window >= 0))
+    qd, kd, vd, cqd, ckd = to_dev(q, k, v, cu_q, cu_k)
+    o, lse = prefill_varlen(qd, kd, vd, cqd, ckd, 500, causal=causal, scale=scale, window_left=window)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    starts = cu_q[:-1].tolist()
+    rows = sorted({r for s, (nq, _) in zip(starts, lens) for r in (s, s + nq // 2, s + nq - 1)} |
+                  set(range(starts[8], starts[8] + 16)))
+    ro, rl = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, scale, window_left=window, rows=rows)
+    check_bf16(o[rows], ro[rows], "wide varlen short+long o")
+    err = np.abs(f64(lse[:, rows]) - rl[:, rows]).max()
+    assert err <= BF16_LSE_MAX_ABS, f"wide varlen short+long lse max-abs {err:.3e}"
+
+
 @pytest.mark.parametrize("causal,n", [(True, 16500), (False, 8300)])
 def test_wide_varlen_single_sequence_equals_dense(causal, n):
     """One full-length sequence long enough for the 8-wave launch: packed and

@@ -76,10 +76,10 @@ namespace {
 // per tile (compile-time).  Eight waves (256 query rows sharing each K/V
 // tile, one workgroup per CU, four ring slots) halve the L2 -> LDS traffic
 // and gain ~2% when the average query row sees 4K keys or more, but lose
-// 2-20% on shorter rows (causal 2K-4K, 1K-key windows), where one workgroup
-// per CU leaves its prologue and the wider causal diagonal exposed.  The launcher picks the
-// width per call (FA_PREFILL_WAVES=4 or 8 forces one, for testing).  32-key
-// tiles are ~3% slower.
+// 2-20% on shorter rows (causal MHA 2K and 4K, 1K-key windows), where one
+// workgroup per CU leaves its prologue and the wider causal diagonal
+// exposed.  The launcher picks the width per call (FA_PREFILL_WAVES=4 or 8
+// forces one, for testing).  32-key tiles are ~3% slower.
 #ifndef FA_PREFILL_WAVES
 #define FA_PREFILL_WAVES 0
 #endif
